@@ -1,0 +1,201 @@
+"""Oracle decoding loops and the commit rule (float64) -- test infrastructure.
+
+Block diffusion (MLX guide, sec. 6; Module 12, sec. 14): the prompt is
+prefilled causally into the KV cache; each block of L positions starts fully
+masked and is denoised by repeated bidirectional passes against the cached
+prefix; after each pass the commit rule unmasks some positions and leaves the
+rest masked; when no mask is left the finished block goes through one causal
+pass whose keys/values are appended to the cache.
+
+Commit rule (MLX guide, sec. 5.2 native sampler and sec. 6; NLD tutorial,
+sec. 3.1; DiffusionGemma, BlockRefinementScheduler), with these readings:
+  * candidates are each masked position's argmax, ranked by confidence, ties
+    to the smaller position (Module 12, sec. 12 contract);
+  * A = {masked j : conf_j > tau} (strictly above the threshold);
+  * at least q = min(quota, #masked) positions open per step; on the last
+    allowed step every remaining mask is committed (forced completion);
+  * n = max(|A|, q) top-ranked positions are committed; the others stay masked;
+  * committed positions never change (no editing).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+from .model import KVCache, forward, head_logits, confidence
+
+
+def commit(conf, argmax, canvas, masked, tau, quota, step, max_steps):
+    """Apply the commit rule to one row.
+
+    conf, argmax: per-position confidence and candidate ([L]); only masked
+    positions are read.  canvas [L] ints, masked [L] bools.  ``step`` is the
+    number of denoise steps this row has already taken in the block.
+    Returns (canvas, masked, step, n_committed) as new arrays.  A row with no
+    mask left is frozen: nothing changes and the step count stays.
+    """
+    canvas = np.array(canvas, copy=True)
+    masked = np.array(masked, dtype=bool, copy=True)
+    idx = np.flatnonzero(masked)
+    if idx.size == 0:
+        return canvas, masked, step, 0
+    conf = np.asarray(conf)
+    above = [j for j in idx if conf[j] > tau]
+    if step >= max_steps - 1:
+        q = idx.size                      # forced completion on the last allowed step
+    else:
+        q = min(int(quota), idx.size)
+    n = max(len(above), q)
+    ranked = sorted(idx.tolist(), key=lambda j: (-float(conf[j]), j))
+    for j in ranked[:n]:
+        canvas[j] = argmax[j]
+        masked[j] = False
+    return canvas, masked, step + 1, n
+
+
+def commit_batch(conf, argmax, canvas, masked, tau, quota, steps, max_steps):
+    """Row-wise ``commit`` over a batch; tau and quota may be scalars or per row.
+
+    Returns (canvas, masked, steps, n_committed, n_left) as new arrays.
+    """
+    b = np.asarray(canvas).shape[0]
+    tau = np.broadcast_to(np.asarray(tau), (b,))
+    quota = np.broadcast_to(np.asarray(quota), (b,))
+    out_c, out_m, out_s, out_n = [], [], [], []
+    for r in range(b):
+        c, m, s, n = commit(conf[r], argmax[r], canvas[r], masked[r], tau[r], quota[r],
+                            int(steps[r]), max_steps)
+        out_c.append(c)
+        out_m.append(m)
+        out_s.append(s)
+        out_n.append(n)
+    masked_new = np.array(out_m)
+    return (np.array(out_c), masked_new, np.array(out_s), np.array(out_n),
+            masked_new.sum(axis=1))
+
+
+def linear_mask_schedule(length: int, steps: int):
+    """Target mask counts m_s = ceil(N (S - s) / S), s = 0..S (Module 12, sec. 6)."""
+    if length <= 0 or steps <= 0:
+        raise ValueError("length and steps must be positive")
+    return tuple(-(-(length * (steps - s)) // steps) for s in range(steps + 1))
+
+
+def sample_fixed_schedule(predict, length, steps, mask_id):
+    """Greedy confidence reveal opening exactly the scheduled number of positions per call.
+
+    ``predict(tokens, step)`` returns logits [L, V]; one call per iteration.
+    Uses the commit rule with an unreachable threshold and the per-step quota
+    m_{s-1} - m_s, so it is the Module 12 sec. 9/12 sampler expressed through
+    ``commit``.  Returns (tokens, trace) with trace = [(opened positions, tokens)].
+    """
+    sched = linear_mask_schedule(length, steps)
+    tokens = np.full(length, mask_id, dtype=np.int64)
+    masked = np.ones(length, dtype=bool)
+    trace = []
+    for s in range(1, steps + 1):
+        logits = np.asarray(predict(tokens.copy(), s), dtype=np.float64)
+        conf, arg = confidence(logits)
+        before = masked.copy()
+        quota = sched[s - 1] - sched[s]
+        tokens, masked, _, _ = commit(conf, arg, tokens, masked, np.inf, quota, s - 1,
+                                      steps + 1)
+        opened = tuple(np.flatnonzero(before & ~masked).tolist())
+        trace.append((opened, tokens.copy()))
+    return tokens, trace
+
+
+def prefill(w, shape, prompt):
+    """Causal pass over the prompt; returns (cache, final residual stream [T, d])."""
+    cache = KVCache(shape)
+    x = forward(w, shape, prompt, cache, mode="causal", write_cache=True)
+    return cache, x
+
+
+def denoise_logits(w, shape, cache, canvas):
+    """One bidirectional-block pass of the canvas against the cached prefix; no cache write."""
+    x = forward(w, shape, canvas, cache, mode="block", write_cache=False)
+    return head_logits(w, shape, x)
+
+
+def append_block(w, shape, cache, block):
+    """Causal pass of the finished block; its keys/values are appended to the cache."""
+    return forward(w, shape, block, cache, mode="causal", write_cache=True)
+
+
+@dataclass
+class BlockStats:
+    """Counters of the MLX guide, sec. 9 (denoise and post-block forwards, tokens per forward)."""
+    denoise_nfe: int = 0
+    post_block_nfe: int = 0
+    blocks: int = 0
+    accepted_tokens: int = 0
+    masked_rows_scored: int = 0
+    steps_per_block: list = field(default_factory=list)
+    trace: list = field(default_factory=list)
+
+    @property
+    def tokens_per_denoise_forward(self) -> float:
+        return self.accepted_tokens / max(self.denoise_nfe, 1)
+
+
+def generate_block_diffusion(w, shape, prompt, gen_length, block_length, max_steps,
+                             tau=0.9, quota=1, keep_trace=False):
+    """Block-diffusion decoding of one sequence; returns (generated tokens, stats, cache).
+
+    All block positions start as the mask id (no anchor token).  A generation
+    length that is not a multiple of the block length is rounded up.
+    """
+    cache, _ = prefill(w, shape, prompt)
+    n_blocks = -(-gen_length // block_length)
+    out = []
+    st = BlockStats()
+    for _ in range(n_blocks):
+        canvas = np.full(block_length, shape.mask_id, dtype=np.int64)
+        masked = np.ones(block_length, dtype=bool)
+        step = 0
+        while masked.any():
+            logits = denoise_logits(w, shape, cache, canvas)
+            st.masked_rows_scored += int(masked.sum())
+            conf, arg = confidence(logits)
+            canvas, masked_new, step, n = commit(conf, arg, canvas, masked, tau, quota,
+                                                 step, max_steps)
+            if keep_trace:
+                st.trace.append((tuple(np.flatnonzero(masked & ~masked_new).tolist()),
+                                 canvas.copy()))
+            masked = masked_new
+            st.denoise_nfe += 1
+            st.accepted_tokens += n
+        append_block(w, shape, cache, canvas)
+        st.post_block_nfe += 1
+        st.blocks += 1
+        st.steps_per_block.append(step)
+        out.extend(canvas.tolist())
+    return np.array(out, dtype=np.int64), st, cache
+
+
+def generate_ar(w, shape, prompt, n_new):
+    """Greedy causal decoding with the KV cache (MLX guide, sec. 3.1 autoregressive path)."""
+    cache = KVCache(shape)
+    x = forward(w, shape, prompt, cache, mode="causal", write_cache=True)
+    out = []
+    for i in range(n_new):
+        _, arg = confidence(head_logits(w, shape, x[-1:]))
+        tok = int(arg[0])
+        out.append(tok)
+        if i + 1 < n_new:
+            x = forward(w, shape, np.array([tok]), cache, mode="causal", write_cache=True)
+    return np.array(out, dtype=np.int64)
+
+
+def generate_ar_recompute(w, shape, prompt, n_new):
+    """Greedy decoding that re-runs the whole sequence causally each step, without a cache."""
+    seq = list(np.asarray(prompt).tolist())
+    out = []
+    for _ in range(n_new):
+        x = forward(w, shape, np.array(seq), None, mode="causal")
+        _, arg = confidence(head_logits(w, shape, x[-1:]))
+        out.append(int(arg[0]))
+        seq.append(int(arg[0]))
+    return np.array(out, dtype=np.int64)
