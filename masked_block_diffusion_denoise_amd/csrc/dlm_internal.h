@@ -1,0 +1,86 @@
+// Host-side launchers of the libdlm kernels.  Every launcher enqueues work on
+// `stream` and returns the launch status; none allocates, frees or synchronises.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dlm {
+
+typedef uint16_t bf16_t;  // raw bf16 bits in memory
+
+// ---------------------------------------------------------------- GEMM ----
+// C = A[M][K] * W[N][K]^T with bf16 operands and fp32 accumulation.
+enum GemmEpilogue : int {
+  EPI_STORE_BF16 = 0,  // out bf16 [M][ldc]
+  EPI_RESID_F32 = 1,   // out fp32 [M][ldc] += acc (residual stream)
+  EPI_SWIGLU = 2,      // W rows gate/up interleaved in 16-row groups; out bf16 [M][N/2] = silu(g)*u
+  EPI_HEAD = 3,        // per (row, vocab tile) partial max / sum exp / argmax; optional fp32 logits
+};
+
+struct GemmArgs {
+  const void* a;        // bf16 [M][lda]
+  const void* w;        // bf16 [N][K]
+  void* out;            // see epilogue
+  int M, N, K;
+  int lda, ldc;
+  const int* m_dev;     // optional device row count (rows >= *m_dev are skipped); M is the bound
+  // EPI_HEAD only
+  void* partials;       // MaxSumIdx-like records [n_tiles][M]
+  float* logits;        // optional fp32 [rows][N]
+  const int* logit_rows; // optional: logits of result row m go to row logit_rows[m]
+  int mask_id;
+  int* nonfinite;       // device counter, incremented on non-finite logits
+  // split-K scratch (skinny path)
+  float* splitk_ws;     // fp32 [ks][M][N]
+  int* splitk_cnt;      // int [N / 64], zero on entry, left zero on exit
+};
+
+size_t gemm_splitk_ws_floats(int M, int N, int K);  // fp32 elements of split-K scratch
+int gemm_head_tile_n(int M);                       // vocab columns per EPI_HEAD partial
+hipError_t gemm(const GemmArgs& g, GemmEpilogue epi, hipStream_t s);
+
+// --------------------------------------------------------- attention ----
+struct AttnArgs {
+  const void* q;          // bf16, row m = b*Lq + j, head h at q[m*ldq + h*hd]
+  int ldq;
+  const void* kc;         // bf16 K cache of this layer [B][G][cap][hd]
+  const void* vc;         // bf16 V cache of this layer [B][G][cap/16][hd][16]
+  void* o;                // bf16 [B*Lq][H*hd]
+  const int* prefix;      // device [B] or null
+  int pos_offset;         // query j of row b sits at prefix[b] + pos_offset + j
+  int B, Lq, H, G, hd, cap;
+  int causal;             // 0: every key < prefix+pos_offset+Lq visible; 1: key <= query position
+  int max_kv;             // host bound on prefix[b] + pos_offset + Lq
+  float* part_o;          // fp32 [splits][B*Lq][H][hd]
+  float* part_ml;         // fp32 [splits][B*Lq][H][2]
+};
+int attn_splits(const AttnArgs& a, int* chunk_out);
+size_t attn_partial_floats(int splits, int rows, int H, int hd);
+hipError_t attention(const AttnArgs& a, hipStream_t s);
+
+// ------------------------------------------------------------ small ----
+hipError_t commit(const float* conf, const int* argmax, int* canvas, uint8_t* masked, int B, int L,
+                  const float* tau, const int* quota, int* steps, int max_steps, int* n_committed,
+                  int* n_left, hipStream_t s);
+// row m = b*Lq + j takes token tokens[b*tok_ld + j]
+hipError_t embed_norm(const int* tokens, int M, int Lq, int tok_ld, const void* embed, int V, int d,
+                      const void* gain, float eps, float* x, void* xn, int* bad_token, hipStream_t s);
+hipError_t rmsnorm(const float* x, int M, int d, const void* gain, float eps, void* xn,
+                   const int* rows, const int* m_dev, hipStream_t s);
+hipError_t rope_table(const int* prefix, int pos_offset, int B, int Lq, int hd, float base, float2* tab,
+                      hipStream_t s);
+hipError_t rope_kv(void* qkv, int M, int Lq, int H, int G, int hd, const float2* tab, void* kc, void* vc,
+                   const int* prefix, int pos_offset, int cap, hipStream_t s);
+hipError_t masked_rows(const uint8_t* masked, int M, int* rows, int* count, hipStream_t s);
+hipError_t head_merge(const void* partials, int n_tiles, int M, const int* rows, const int* m_dev,
+                      float* conf, int* argmax, int total_rows, hipStream_t s);
+hipError_t fill_i32(int* p, int n, int v, hipStream_t s);
+hipError_t fill_f32(float* p, int n, float v, hipStream_t s);
+// prefix[b] = (add ? prefix[b] : 0) + value
+hipError_t set_prefix(int* prefix, int B, int add, int value, hipStream_t s);
+// rows[b] = b*stride + start
+hipError_t strided_rows(int* rows, int n, int start, int stride, hipStream_t s);
+
+}  // namespace dlm

@@ -1,0 +1,386 @@
+// Small kernels of the denoising path: commit/remask, embedding gather + RMSNorm,
+// RMSNorm, RoPE table and RoPE + KV-cache write, masked-row compaction, the
+// cross-tile merge of the LM-head partials, and fills.
+#include "dlm_device.h"
+#include "dlm_internal.h"
+
+namespace dlm {
+
+// ------------------------------------------------------------ commit ----
+// Commit rule (MLX-VLM Nemotron Labs Diffusion guide, sec. 5.2 native sampler and
+// sec. 6; DiffusionGemma docs, BlockRefinementScheduler): per row, A = masked
+// positions with conf > tau; q = #masked on the last allowed step, else
+// min(quota, #masked); the top max(|A|, q) masked positions by (-conf, position)
+// take their argmax token and leave the mask; the others stay masked.  Rows with
+// no mask left are frozen.  One wavefront per row (L <= 64).
+__global__ void __launch_bounds__(256) k_commit(const float* __restrict__ conf,
+                                                const int* __restrict__ argmax, int* __restrict__ canvas,
+                                                uint8_t* __restrict__ masked, int B, int L,
+                                                const float* __restrict__ tau,
+                                                const int* __restrict__ quota, int* __restrict__ steps,
+                                                int max_steps, int* __restrict__ n_committed,
+                                                int* __restrict__ n_left) {
+  const int lane = threadIdx.x & 63;
+  const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (b >= B) return;  // uniform per wavefront
+  const size_t base = static_cast<size_t>(b) * L;
+  const bool in = lane < L;
+  const bool mk = in && masked[base + lane] != 0;
+  const float c = in ? conf[base + lane] : 0.f;
+  const unsigned long long mball = __ballot(mk);
+  const int cnt = __popcll(mball);
+  if (cnt == 0) {
+    if (lane == 0) {
+      n_committed[b] = 0;
+      n_left[b] = 0;
+    }
+    return;
+  }
+  const int st = steps[b];
+  const float t = tau[b];
+  const int above = __popcll(__ballot(mk && c > t));
+  const int q = (st >= max_steps - 1) ? cnt : min(quota[b], cnt);
+  const int n = max(above, q);
+  int rank = 0;
+  for (int i = 0; i < L; ++i) {
+    const float ci = __shfl(c, i, WAVE);
+    const bool mi = (mball >> i) & 1ull;
+    rank += (mi && (ci > c || (ci == c && i < lane))) ? 1 : 0;
+  }
+  if (mk && rank < n) {
+    canvas[base + lane] = argmax[base + lane];
+    masked[base + lane] = 0;
+  }
+  if (lane == 0) {
+    steps[b] = st + 1;
+    n_committed[b] = n;
+    n_left[b] = cnt - n;
+  }
+}
+
+hipError_t commit(const float* conf, const int* argmax, int* canvas, uint8_t* masked, int B, int L,
+                  const float* tau, const int* quota, int* steps, int max_steps, int* n_committed,
+                  int* n_left, hipStream_t s) {
+  hipLaunchKernelGGL(k_commit, dim3((B + 3) / 4), dim3(256), 0, s, conf, argmax, canvas, masked, B, L,
+                     tau, quota, steps, max_steps, n_committed, n_left);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ RMSNorm ----
+__device__ __forceinline__ float block_sum_256(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) t += red[i];
+  __syncthreads();
+  return t;
+}
+
+__device__ __forceinline__ void unpack8(u32x4 v, float* f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(v[i] << 16);
+    f[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+  }
+}
+
+// x[m] = E[tok[m]] (fp32) and xn[m] = RMSNorm(x[m]) * g (bf16).  RMSNorm is
+// x / sqrt(mean(x^2) + eps) * g.  Out-of-range tokens read as zeros and are counted.
+__global__ void __launch_bounds__(256) k_embed_norm(const int* __restrict__ tokens, int Lq, int tok_ld,
+                                                    const bf16_t* __restrict__ E, int V, int d,
+                                                    const bf16_t* __restrict__ g, float eps,
+                                                    float* __restrict__ x, bf16_t* __restrict__ xn,
+                                                    int* __restrict__ bad) {
+  __shared__ float red[4];
+  const int m = blockIdx.x;
+  const int t = tokens[static_cast<size_t>(m / Lq) * tok_ld + m % Lq];
+  const bool ok = t >= 0 && t < V;
+  if (!ok && threadIdx.x == 0 && bad) atomicAdd(bad, 1);
+  const bf16_t* row = E + static_cast<size_t>(ok ? t : 0) * d;
+  float ss = 0.f;
+  for (int c = threadIdx.x; c < d / 8; c += 256) {
+    float f[8];
+    u32x4 v = ok ? ld16(row + c * 8) : u32x4{0, 0, 0, 0};
+    unpack8(v, f);
+    float* xo = x + static_cast<size_t>(m) * d + c * 8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      xo[i] = f[i];
+      ss += f[i] * f[i];
+    }
+  }
+  const float rstd = rsqrtf(block_sum_256(ss, red) / d + eps);
+  for (int c = threadIdx.x; c < d / 8; c += 256) {
+    float f[8], gg[8];
+    u32x4 v = ok ? ld16(row + c * 8) : u32x4{0, 0, 0, 0};
+    unpack8(v, f);
+    unpack8(ld16(g + c * 8), gg);
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(f[2 * i] * rstd * gg[2 * i], f[2 * i + 1] * rstd * gg[2 * i + 1]);
+    st16(xn + static_cast<size_t>(m) * d + c * 8, o);
+  }
+}
+
+hipError_t embed_norm(const int* tokens, int M, int Lq, int tok_ld, const void* embed, int V, int d,
+                      const void* gain, float eps, float* x, void* xn, int* bad_token, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_embed_norm, dim3(M), dim3(256), 0, s, tokens, Lq, tok_ld, static_cast<const bf16_t*>(embed), V,
+                     d, static_cast<const bf16_t*>(gain), eps, x, static_cast<bf16_t*>(xn), bad_token);
+  return hipGetLastError();
+}
+
+// xn[i] = RMSNorm(x[rows ? rows[i] : i]) * g; rows i >= *m_dev are skipped.
+__global__ void __launch_bounds__(256) k_rmsnorm(const float* __restrict__ x, int d,
+                                                 const bf16_t* __restrict__ g, float eps,
+                                                 bf16_t* __restrict__ xn, const int* __restrict__ rows,
+                                                 const int* __restrict__ m_dev) {
+  __shared__ float red[4];
+  const int i = blockIdx.x;
+  if (m_dev && i >= *m_dev) return;
+  const int src = rows ? rows[i] : i;
+  const float* xr = x + static_cast<size_t>(src) * d;
+  float ss = 0.f;
+  for (int c = threadIdx.x; c < d / 4; c += 256) {
+    const float4 v = reinterpret_cast<const float4*>(xr)[c];
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  const float rstd = rsqrtf(block_sum_256(ss, red) / d + eps);
+  for (int c = threadIdx.x; c < d / 8; c += 256) {
+    const float4 v0 = reinterpret_cast<const float4*>(xr)[2 * c];
+    const float4 v1 = reinterpret_cast<const float4*>(xr)[2 * c + 1];
+    float gg[8];
+    unpack8(ld16(g + c * 8), gg);
+    u32x4 o;
+    o[0] = pack_bf16x2(v0.x * rstd * gg[0], v0.y * rstd * gg[1]);
+    o[1] = pack_bf16x2(v0.z * rstd * gg[2], v0.w * rstd * gg[3]);
+    o[2] = pack_bf16x2(v1.x * rstd * gg[4], v1.y * rstd * gg[5]);
+    o[3] = pack_bf16x2(v1.z * rstd * gg[6], v1.w * rstd * gg[7]);
+    st16(xn + static_cast<size_t>(i) * d + c * 8, o);
+  }
+}
+
+hipError_t rmsnorm(const float* x, int M, int d, const void* gain, float eps, void* xn, const int* rows,
+                   const int* m_dev, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_rmsnorm, dim3(M), dim3(256), 0, s, x, d, static_cast<const bf16_t*>(gain), eps,
+                     static_cast<bf16_t*>(xn), rows, m_dev);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- RoPE ----
+// Rotation angles for row m = b*Lq + j at absolute position p = prefix[b] + off + j:
+// pair i of a head (components i and i + hd/2) turns by p * base^(-2i/hd).  The
+// angle is formed in double precision (positions reach 1e5 and beyond), its
+// cosine and sine are stored as fp32 and shared by every head and layer.
+__global__ void k_rope_table(const int* __restrict__ prefix, int off, int Lq, int half, double log_base,
+                             float2* __restrict__ tab, int total) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= total) return;
+  const int m = e / half, i = e % half;
+  const int b = m / Lq, j = m % Lq;
+  const double p = static_cast<double>((prefix ? prefix[b] : 0) + off + j);
+  const double freq = exp(-2.0 * i / (2.0 * half) * log_base);
+  double sn, cs;
+  sincos(p * freq, &sn, &cs);
+  tab[e] = make_float2(static_cast<float>(cs), static_cast<float>(sn));
+}
+
+hipError_t rope_table(const int* prefix, int pos_offset, int B, int Lq, int hd, float base, float2* tab,
+                      hipStream_t s) {
+  const int total = B * Lq * (hd / 2);
+  if (total <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_rope_table, dim3((total + 255) / 256), dim3(256), 0, s, prefix, pos_offset, Lq, hd / 2,
+                     log(static_cast<double>(base)), tab, total);
+  return hipGetLastError();
+}
+
+// Rotate the query heads in place and write the rotated keys and the values of
+// every row into the cache slot of its position.  qkv row layout: H query heads,
+// then G key heads, then G value heads, each hd wide.  Each thread handles four
+// rotation pairs of one head.  K cache [B][G][cap][hd]; V cache
+// [B][G][cap/16][hd][16] (blocks of 16 positions, position fastest).
+__global__ void __launch_bounds__(256) k_rope_kv(bf16_t* __restrict__ qkv, int Lq, int H, int G, int hd,
+                                                 const float2* __restrict__ tab, bf16_t* __restrict__ kc,
+                                                 bf16_t* __restrict__ vc, const int* __restrict__ prefix,
+                                                 int off, int cap) {
+  const int m = blockIdx.x;
+  const int half = hd / 2, quads = half / 4;
+  const int nh = H + 2 * G;
+  const int b = m / Lq, j = m % Lq;
+  const int pos = (prefix ? prefix[b] : 0) + off + j;
+  const bool slot_ok = pos >= 0 && pos < cap;
+  bf16_t* row = qkv + static_cast<size_t>(m) * nh * hd;
+  for (int t = threadIdx.x; t < nh * quads; t += blockDim.x) {
+    const int h = t / quads, i0 = (t % quads) * 4;
+    bf16_t* hp = row + h * hd;
+    if (h >= H + G) {  // value head: copy to the blocked V cache
+      if (!slot_ok) continue;
+      const int g = h - H - G;
+      bf16_t* vb = vc + ((static_cast<size_t>(b) * G + g) * (cap / 16) + pos / 16) * hd * 16 + pos % 16;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        vb[(i0 + u) * 16] = hp[i0 + u];
+        vb[(i0 + u + half) * 16] = hp[i0 + u + half];
+      }
+      continue;
+    }
+    const u32x2 lo = *reinterpret_cast<const u32x2*>(hp + i0);
+    const u32x2 hi = *reinterpret_cast<const u32x2*>(hp + i0 + half);
+    float x1[4] = {__uint_as_float(lo[0] << 16), __uint_as_float(lo[0] & 0xffff0000u),
+                   __uint_as_float(lo[1] << 16), __uint_as_float(lo[1] & 0xffff0000u)};
+    float x2[4] = {__uint_as_float(hi[0] << 16), __uint_as_float(hi[0] & 0xffff0000u),
+                   __uint_as_float(hi[1] << 16), __uint_as_float(hi[1] & 0xffff0000u)};
+    float y1[4], y2[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float2 cs = tab[static_cast<size_t>(m) * half + i0 + u];
+      y1[u] = x1[u] * cs.x - x2[u] * cs.y;
+      y2[u] = x2[u] * cs.x + x1[u] * cs.y;
+    }
+    const u32x2 olo = {pack_bf16x2(y1[0], y1[1]), pack_bf16x2(y1[2], y1[3])};
+    const u32x2 ohi = {pack_bf16x2(y2[0], y2[1]), pack_bf16x2(y2[2], y2[3])};
+    if (h < H) {
+      *reinterpret_cast<u32x2*>(hp + i0) = olo;
+      *reinterpret_cast<u32x2*>(hp + i0 + half) = ohi;
+    } else if (slot_ok) {
+      const int g = h - H;
+      bf16_t* kp = kc + ((static_cast<size_t>(b) * G + g) * cap + pos) * hd;
+      *reinterpret_cast<u32x2*>(kp + i0) = olo;
+      *reinterpret_cast<u32x2*>(kp + i0 + half) = ohi;
+    }
+  }
+}
+
+hipError_t rope_kv(void* qkv, int M, int Lq, int H, int G, int hd, const float2* tab, void* kc, void* vc,
+                   const int* prefix, int pos_offset, int cap, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_rope_kv, dim3(M), dim3(256), 0, s, static_cast<bf16_t*>(qkv), Lq, H, G, hd, tab,
+                     static_cast<bf16_t*>(kc), static_cast<bf16_t*>(vc), prefix, pos_offset, cap);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------ masked rows ----
+// rows[0..count) = indices m with masked[m] != 0, ascending; count[0] = how many.
+__global__ void __launch_bounds__(1024) k_masked_rows(const uint8_t* __restrict__ masked, int M,
+                                                      int* __restrict__ rows, int* __restrict__ count) {
+  __shared__ int wsum[16];
+  __shared__ int carry;
+  if (threadIdx.x == 0) carry = 0;
+  __syncthreads();
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int base = 0; base < M; base += 1024) {
+    const int m = base + threadIdx.x;
+    const int f = (m < M && masked[m]) ? 1 : 0;
+    const unsigned long long bal = __ballot(f);
+    const int before = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) wsum[w] = __popcll(bal);
+    __syncthreads();
+    int off = carry;
+    for (int i = 0; i < w; ++i) off += wsum[i];
+    if (f) rows[off + before] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int t = 0;
+      for (int i = 0; i < 16; ++i) t += wsum[i];
+      carry += t;
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) count[0] = carry;
+}
+
+hipError_t masked_rows(const uint8_t* masked, int M, int* rows, int* count, hipStream_t s) {
+  hipLaunchKernelGGL(k_masked_rows, dim3(1), dim3(1024), 0, s, masked, M, rows, count);
+  return hipGetLastError();
+}
+
+// --------------------------------------------------------- head merge ----
+// Per scored row: merge the per-vocab-tile (max, sum exp, argmax) partials in a
+// fixed order, then conf = 1 / sum_v exp(l_v - max) and the argmax (lowest id on
+// ties) go to position rows[i] of the canvas.
+__global__ void __launch_bounds__(256) k_head_merge(const float4* __restrict__ part, int n_tiles, int M,
+                                                    const int* __restrict__ rows,
+                                                    const int* __restrict__ m_dev, float* __restrict__ conf,
+                                                    int* __restrict__ argmax) {
+  __shared__ float sm[256], ss[256];
+  __shared__ int si[256];
+  const int i = blockIdx.x;
+  if (m_dev && i >= *m_dev) return;
+  MaxSumIdx acc{-INFINITY, 0.f, 0x7fffffff};
+  for (int t = threadIdx.x; t < n_tiles; t += 256) {
+    const float4 p = part[static_cast<size_t>(t) * M + i];
+    acc = msi_combine(acc, MaxSumIdx{p.x, p.y, __float_as_int(p.z)});
+  }
+  sm[threadIdx.x] = acc.m;
+  ss[threadIdx.x] = acc.s;
+  si[threadIdx.x] = acc.idx;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) {
+      MaxSumIdx a{sm[threadIdx.x], ss[threadIdx.x], si[threadIdx.x]};
+      MaxSumIdx c{sm[threadIdx.x + w], ss[threadIdx.x + w], si[threadIdx.x + w]};
+      a = msi_combine(a, c);
+      sm[threadIdx.x] = a.m;
+      ss[threadIdx.x] = a.s;
+      si[threadIdx.x] = a.idx;
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const int dst = rows ? rows[i] : i;
+    conf[dst] = 1.0f / ss[0];
+    argmax[dst] = si[0];
+  }
+}
+
+hipError_t head_merge(const void* partials, int n_tiles, int M, const int* rows, const int* m_dev,
+                      float* conf, int* argmax, int total_rows, hipStream_t s) {
+  if (total_rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_head_merge, dim3(total_rows), dim3(256), 0, s, static_cast<const float4*>(partials),
+                     n_tiles, M, rows, m_dev, conf, argmax);
+  return hipGetLastError();
+}
+
+// --------------------------------------------------------------- fills ----
+__global__ void k_fill_i32(int* p, int n, int v) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+__global__ void k_fill_f32(float* p, int n, float v) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+__global__ void k_set_prefix(int* prefix, int B, int add, int value) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < B) prefix[b] = (add ? prefix[b] : 0) + value;
+}
+
+hipError_t fill_i32(int* p, int n, int v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fill_i32, dim3((n + 255) / 256), dim3(256), 0, s, p, n, v);
+  return hipGetLastError();
+}
+hipError_t fill_f32(float* p, int n, float v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fill_f32, dim3((n + 255) / 256), dim3(256), 0, s, p, n, v);
+  return hipGetLastError();
+}
+hipError_t set_prefix(int* prefix, int B, int add, int value, hipStream_t s) {
+  hipLaunchKernelGGL(k_set_prefix, dim3((B + 255) / 256), dim3(256), 0, s, prefix, B, add, value);
+  return hipGetLastError();
+}
+__global__ void k_strided_rows(int* rows, int n, int start, int stride) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) rows[i] = i * stride + start;
+}
+hipError_t strided_rows(int* rows, int n, int start, int stride, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_strided_rows, dim3((n + 255) / 256), dim3(256), 0, s, rows, n, start, stride);
+  return hipGetLastError();
+}
+
+}  // namespace dlm

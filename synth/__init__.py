@@ -169,20 +169,23 @@ def hidden_rows(rows: int, d: int, seed: int = 0, std: float = 1.0) -> np.ndarra
     return normal(seed, K_HIDDEN, (rows, d), std)
 
 
-def planted_hidden(lm_head: np.ndarray, rows: int, seed: int = 0,
-                   gains=(2.0, 40.0), noise: float = 0.3):
-    """Hidden rows aligned with one head row each, so max-probabilities spread over (0, 1).
+def planted_hidden(lm_head: np.ndarray, rows: int, seed: int = 0):
+    """Hidden rows aimed at one head row each, so max-probabilities spread over (0, 1).
 
-    Row r is ``alpha_r * W[t_r] / |W[t_r]| + noise * n_r`` with t_r a random token
-    and alpha_r log-uniform in ``gains``.  Returns (hidden float32 [R, d], targets).
+    Row r is ``delta_r * W[t_r] / |W[t_r]|^2 + n_r``: its logit for token t_r
+    exceeds the others by about delta_r (uniform in [0, ln V + 6]), and the noise
+    n_r gives the other logits a spread of about one unit.  Returns
+    (hidden float32 [R, d] bf16-rounded, targets int32 [R]).
     """
     g = rng(seed, K_HIDDEN, 7)
     v, d = lm_head.shape
     t = g.integers(0, v, size=rows)
-    alpha = np.exp(g.uniform(np.log(gains[0]), np.log(gains[1]), size=rows))
+    delta = g.uniform(0.0, np.log(v) + 6.0, size=rows)
     w = lm_head[t].astype(np.float64)
-    w = w / np.sqrt((w * w).sum(axis=1, keepdims=True))
-    h = alpha[:, None] * w * np.sqrt(d) + noise * g.standard_normal((rows, d))
+    w2 = (w * w).sum(axis=1, keepdims=True)
+    col_rms = np.sqrt(np.mean(lm_head[: min(v, 4096)].astype(np.float64) ** 2))
+    noise = g.standard_normal((rows, d)) / (col_rms * np.sqrt(d))
+    h = delta[:, None] * w / w2 + noise
     return bf16_round(h.astype(np.float32)), t.astype(np.int32)
 
 

@@ -1,0 +1,203 @@
+"""Whole denoising path through the C ABI vs the oracle.
+
+* Tiny model (2 layers, d=128, vocab 1024): prefill cache, teacher-forced
+  denoise steps (conf within 1e-2, logits within 2e-2 relative RMS, argmax equal
+  where the top-1 margin exceeds 5e-2), commit bit-exact on the oracle's
+  (conf, argmax), append cache equal to the oracle's.
+* Free-running block diffusion with a confident head: committed tokens equal the
+  oracle's up to the first decision the oracle itself takes within 5e-2.
+* One decoder layer at 8B-class shapes with the 131072-vocab head over a 4096-key
+  N(0,1) prefix, batch 1 and 32 (sampled rows at 32).
+"""
+import ctypes as C
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_helpers import announce, f32, host, i32, p, rel_rms, stream, sync, u8
+from masked_block_diffusion_denoise_amd import _lib as L
+from masked_block_diffusion_denoise_amd import runtime as R
+
+pytestmark = pytest.mark.gpu
+
+TINY = synth.TINY
+
+
+def make(shape, w):
+    return R.DlmModel.from_arrays(R.ModelConfig.of(shape), w)
+
+
+def cache_close(sess, cache, b, upto, tol=1e-2):
+    kl = host(sess.kv.k_logical().float())
+    vl = host(sess.kv.v_logical().float())
+    for l in range(cache.shape.n_layers):
+        assert rel_rms(kl[l, b, :, :upto], cache.k[l][:, :upto]) < tol, ("k", l)
+        assert rel_rms(vl[l, b, :, :upto], cache.v[l][:, :upto]) < tol, ("v", l)
+
+
+def check_step(conf_g, arg_g, logits_g, logits_o, masked):
+    conf_o, arg_o = oracle.confidence(logits_o)
+    mk = np.flatnonzero(masked)
+    assert np.abs(conf_g[mk] - conf_o[mk]).max() < 1e-2
+    fin = np.isfinite(logits_o[0])
+    for j in mk:
+        assert rel_rms(logits_g[j][fin], logits_o[j][fin]) < 2e-2
+        top2 = np.sort(logits_o[j][fin])[-2:]
+        if top2[1] - top2[0] > 5e-2:
+            assert arg_g[j] == arg_o[j]
+    return conf_o, arg_o
+
+
+def test_tiny_prefill_cache_and_last_token():
+    announce("tiny prefill")
+    w = synth.model_weights(TINY, seed=0, lm_head_gain=20.0)
+    m = make(TINY, w)
+    B, T = 2, 40
+    prompt = synth.prompt(TINY, B, T, seed=1)
+    sess = R.Session(m, B, 128, 16)
+    tp = i32(prompt)
+    last_a = i32(np.zeros(B))
+    last_c = f32(np.zeros(B))
+    # a workspace for 32-row passes forces two prefill passes (32 + 8 positions)
+    ws, n = sess.ws.get(m.workspace_bytes(B * 32, T))
+    L.call("dlm_prefill", m.handle, C.byref(sess.kv.c), p(tp), B, T, p(sess.prefix), p(last_a), p(last_c),
+           p(sess.flags), ws, n, stream())
+    sync()
+    assert (host(sess.prefix) == T).all()
+    for b in range(B):
+        cache, x = oracle.prefill(w, TINY, prompt[b])
+        cache_close(sess, cache, b, T)
+        lg = oracle.head_logits(w, TINY, x[-1:])
+        c, a = oracle.confidence(lg)
+        assert abs(host(last_c)[b] - c[0]) < 1e-2
+        top2 = np.sort(lg[0][np.isfinite(lg[0])])[-2:]
+        if top2[1] - top2[0] > 5e-2:
+            assert host(last_a)[b] == a[0]
+    assert (host(sess.flags) == 0).all()
+
+
+@pytest.mark.parametrize("gain,tau", [(1.0, 0.9), (60.0, 0.9)])
+def test_tiny_teacher_forced_blocks(gain, tau):
+    announce(f"tiny teacher-forced gain={gain}")
+    w = synth.model_weights(TINY, seed=0, lm_head_gain=gain)
+    m = make(TINY, w)
+    prompt = synth.prompt(TINY, 1, 32, seed=0)
+    Lb, max_steps = 16, 16
+    sess = R.Session(m, 1, 128, Lb)
+    sess.prefill(i32(prompt))
+    cache, _ = oracle.prefill(w, TINY, prompt[0])
+    logits = torch.zeros(Lb, TINY.vocab, dtype=torch.float32, device="cuda")
+    tau_t, q_t = f32([tau]), i32([1])
+    for blk in range(2):
+        canvas = np.full(Lb, TINY.mask_id, np.int64)
+        masked = np.ones(Lb, bool)
+        step = 0
+        while masked.any():
+            lo = oracle.denoise_logits(w, TINY, cache, canvas)
+            sess.canvas.copy_(i32(canvas[None]))
+            sess.masked.copy_(u8(masked[None]))
+            sess.denoise_step(logits)
+            sync()
+            conf_o, arg_o = check_step(host(sess.conf)[0], host(sess.argmax)[0], host(logits), lo, masked)
+            # commit on the device fed with the oracle's confidences: bit-exact
+            sess.conf.copy_(f32(conf_o[None]))
+            sess.argmax.copy_(i32(arg_o[None]))
+            sess.steps.fill_(step)
+            sess.commit(tau_t, q_t, max_steps)
+            canvas, masked, step, n = oracle.commit(conf_o.astype(np.float32), arg_o, canvas, masked, tau, 1,
+                                                    step, max_steps)
+            sync()
+            np.testing.assert_array_equal(host(sess.canvas)[0], canvas)
+            np.testing.assert_array_equal(host(sess.masked)[0].astype(bool), masked)
+            assert host(sess.steps)[0] == step and host(sess.n_committed)[0] == n
+        if gain == 1.0:
+            assert step == Lb                    # no confidence reaches 0.9: one commit per step
+        sess.append_block()
+        oracle.append_block(w, TINY, cache, canvas)
+        sync()
+        assert host(sess.prefix)[0] == cache.length
+        cache_close(sess, cache, 0, cache.length)
+    assert (host(sess.flags) == 0).all()
+
+
+def test_tiny_free_running_matches_until_first_ambiguity():
+    announce("tiny free-running")
+    gain, tau, Lb, max_steps = 60.0, 0.9, 16, 16
+    w = synth.model_weights(TINY, seed=0, lm_head_gain=gain)
+    m = make(TINY, w)
+    prompt = synth.prompt(TINY, 1, 32, seed=0)
+    sess = R.Session(m, 1, 128, Lb)
+    out_g, st_g = sess.generate(i32(prompt), 32, max_steps, tau, 1)
+    out_o, st_o, cache = oracle.generate_block_diffusion(w, TINY, prompt[0], 32, Lb, max_steps, tau, 1,
+                                                         keep_trace=True)
+    got = host(out_g)[0]
+    if not np.array_equal(got, out_o):
+        # locate the first step whose decision the oracle takes with less than 5e-2 to spare
+        cache2, _ = oracle.prefill(w, TINY, prompt[0])
+        ambiguous = False
+        for blk in range(2):
+            canvas = np.full(Lb, TINY.mask_id, np.int64)
+            masked = np.ones(Lb, bool)
+            step = 0
+            while masked.any() and not ambiguous:
+                lo = oracle.denoise_logits(w, TINY, cache2, canvas)
+                conf, arg = oracle.confidence(lo)
+                mk = np.flatnonzero(masked)
+                lc = np.sort(np.log(conf[mk]))[::-1]
+                srt = np.sort(lo[mk], axis=1)
+                if (np.abs(conf[mk] - tau).min() < 5e-2 or (len(lc) > 1 and np.min(-np.diff(lc)) < 5e-2)
+                        or (srt[:, -1] - srt[:, -2]).min() < 5e-2):
+                    ambiguous = True
+                canvas, masked, step, _ = oracle.commit(conf, arg, canvas, masked, tau, 1, step, max_steps)
+            if ambiguous:
+                break
+            oracle.append_block(w, TINY, cache2, canvas)
+        assert ambiguous, (got, out_o)
+    assert st_g.denoise_nfe < 32 and st_o.denoise_nfe < 32
+
+
+@pytest.fixture(scope="module")
+def layer8b():
+    announce("generating one 8B-class layer")
+    shape = synth.LAYER_8B
+    w = synth.model_weights(shape, seed=0)
+    return shape, w, make(shape, w)
+
+
+@pytest.mark.parametrize("B,rows", [(1, [0]), (32, [0, 13, 31])])
+def test_layer8b_denoise_step(layer8b, B, rows):
+    announce(f"8B layer denoise B={B}")
+    shape, w, m = layer8b
+    P, Lb = 4096, 32
+    k, v = synth.kv_prefix(shape, B, P, seed=3)
+    canvas, masked = synth.ragged_canvas(shape, B, Lb, seed=3)
+    sess = R.Session(m, B, P + Lb + 64, Lb)
+    sess.kv.write(0, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda())
+    sess.prefix.fill_(P)
+    sess.max_prefix = P
+    sess.canvas.copy_(i32(canvas))
+    sess.masked.copy_(u8(masked))
+    logits = torch.zeros(B * Lb, shape.vocab, dtype=torch.float32, device="cuda") if B == 1 else None
+    sess.denoise_step(logits)
+    sync()
+    conf_g, arg_g = host(sess.conf), host(sess.argmax)
+    lg_all = host(logits).reshape(B, Lb, -1) if logits is not None else None
+    for b in rows:
+        cache = oracle.KVCache(shape)
+        cache.k[0] = k[b].astype(np.float64)
+        cache.v[0] = v[b].astype(np.float64)
+        lo = oracle.denoise_logits(w, shape, cache, canvas[b])
+        conf_o, arg_o = oracle.confidence(lo)
+        mk = np.flatnonzero(masked[b])
+        assert np.abs(conf_g[b, mk] - conf_o[mk]).max() < 1e-2
+        for j in mk:
+            top2 = np.sort(lo[j][np.isfinite(lo[j])])[-2:]
+            if top2[1] - top2[0] > 5e-2:
+                assert arg_g[b, j] == arg_o[j], (b, j)
+            if lg_all is not None:
+                fin = np.isfinite(lo[j])
+                assert rel_rms(lg_all[b, j][fin], lo[j][fin]) < 2e-2
+    assert (host(sess.flags) == 0).all()
