@@ -185,6 +185,19 @@ dlm_status dlm_append_block(const dlm_model* m, const dlm_kv* kv, int32_t* prefi
                             const int32_t* block, int32_t B, int32_t L, int32_t* argmax_out, float* conf_out,
                             int32_t* flags, void* ws, size_t ws_bytes, void* stream);
 
+/* Kernel timing hook (measurement only).  When set, the next calls on this host
+ * thread record `start` (a hipEvent_t) on their stream right before the named
+ * kernel is launched and `stop` right after it; NULL events switch it off.
+ *   DLM_TIMER_LM_HEAD      the fused LM-head GEMM of dlm_denoise_step
+ *   DLM_TIMER_ATTENTION    block attention (with its split merge) of the first layer
+ *   DLM_TIMER_GATE_UP      the SwiGLU gate/up GEMM of the first layer
+ *   DLM_TIMER_DOWN         the down-projection GEMM of the first layer
+ *   DLM_TIMER_QKV          the fused QKV GEMM of the first layer
+ * Errors: INVALID_ARG for an unknown kernel id. */
+enum { DLM_TIMER_LM_HEAD = 0, DLM_TIMER_ATTENTION = 1, DLM_TIMER_GATE_UP = 2, DLM_TIMER_DOWN = 3,
+       DLM_TIMER_QKV = 4, DLM_TIMER_COUNT = 5 };
+dlm_status dlm_set_kernel_timer(int32_t kernel, void* start_event, void* stop_event);
+
 const char* dlm_status_string(dlm_status s);
 /* Detail of the last non-OK return on the calling thread ("" if none). */
 const char* dlm_last_error(void);

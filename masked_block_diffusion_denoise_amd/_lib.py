@@ -16,11 +16,12 @@ STATUS = {0: "DLM_OK", -1: "DLM_ERR_INVALID_ARG", -2: "DLM_ERR_SHAPE", -3: "DLM_
           -4: "DLM_ERR_UNSUPPORTED", -5: "DLM_ERR_HIP", -6: "DLM_ERR_WORKSPACE"}
 
 EPI_STORE_BF16, EPI_RESIDUAL_F32, EPI_SWIGLU = 0, 1, 2
+TIMER_LM_HEAD, TIMER_ATTENTION, TIMER_GATE_UP, TIMER_DOWN, TIMER_QKV = 0, 1, 2, 3, 4
 
 # Every function declared in include/libdlm.h and include/libdlm_ops.h.
 EXPORTS = [
     "dlm_model_create", "dlm_model_destroy", "dlm_workspace_bytes", "dlm_prefill", "dlm_denoise_step",
-    "dlm_commit", "dlm_append_block", "dlm_status_string", "dlm_last_error",
+    "dlm_commit", "dlm_append_block", "dlm_status_string", "dlm_last_error", "dlm_set_kernel_timer",
     "dlm_op_gemm_workspace_bytes", "dlm_op_gemm", "dlm_op_rmsnorm", "dlm_op_rope_workspace_bytes",
     "dlm_op_rope_kv", "dlm_op_attention_workspace_bytes", "dlm_op_attention",
     "dlm_op_lm_head_workspace_bytes", "dlm_op_lm_head",
@@ -64,6 +65,7 @@ _SIGS = {
     "dlm_commit": (i32, [vp, vp, vp, vp, i32, i32, vp, vp, vp, i32, vp, vp, vp]),
     "dlm_append_block": (i32, [vp, C.POINTER(KV), vp, i32, vp, i32, i32, vp, vp, vp, vp, sz, vp]),
     "dlm_status_string": (C.c_char_p, [i32]),
+    "dlm_set_kernel_timer": (i32, [i32, vp, vp]),
     "dlm_last_error": (C.c_char_p, []),
     "dlm_op_gemm_workspace_bytes": (sz, [i32, i32, i32]),
     "dlm_op_gemm": (i32, [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, sz, vp]),
@@ -84,6 +86,9 @@ def load(path: str | None = None):
     if _lib is not None:
         return _lib
     p = path or LIB_PATH
+    # torch ships its own HIP runtime; load it first so that libdlm binds to the
+    # same runtime (one set of device pointers and streams in the process).
+    import torch  # noqa: F401
     if not os.path.exists(p):
         raise RuntimeError(f"{p} is missing: build it with `python -m masked_block_diffusion_denoise_amd.csrc.build` "
                            "(there is no fallback path)")

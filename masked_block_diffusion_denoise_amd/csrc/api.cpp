@@ -28,6 +28,21 @@ namespace {
 
 thread_local char g_err[512] = "";
 
+// Optional event pairs bracketing one kernel launch (measurement only).
+thread_local hipEvent_t g_timer[DLM_TIMER_COUNT][2] = {};
+
+struct TimerScope {
+  int k;
+  hipStream_t s;
+  bool on;
+  TimerScope(int kernel, hipStream_t st, bool enabled = true) : k(kernel), s(st), on(enabled && g_timer[kernel][0]) {
+    if (on) (void)hipEventRecord(g_timer[k][0], s);
+  }
+  ~TimerScope() {
+    if (on) (void)hipEventRecord(g_timer[k][1], s);
+  }
+};
+
 dlm_status fail(dlm_status s, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
@@ -200,7 +215,10 @@ dlm_status run_layers(const dlm_model* m, const dlm_kv* kv, const int32_t* token
     g.K = d;
     g.lda = d;
     g.ldc = nq;
-    DLM_TRY(gemm(g, EPI_STORE_BF16, s), "gemm qkv");
+    {
+      TimerScope t(DLM_TIMER_QKV, s, l == 0);
+      DLM_TRY(gemm(g, EPI_STORE_BF16, s), "gemm qkv");
+    }
     DLM_TRY(rope_kv(p.qkv, R, Lq, c.n_heads, c.n_kv_heads, c.head_dim, p.tab, kc, vc, prefix, pos_offset,
                     kv->capacity, s),
             "rope_kv");
@@ -222,7 +240,10 @@ dlm_status run_layers(const dlm_model* m, const dlm_kv* kv, const int32_t* token
     a.max_kv = max_kv;
     a.part_o = p.part_o;
     a.part_ml = p.part_ml;
-    DLM_TRY(attention(a, s), "attention");
+    {
+      TimerScope t(DLM_TIMER_ATTENTION, s, l == 0);
+      DLM_TRY(attention(a, s), "attention");
+    }
     g.a = p.attn;
     g.w = m->wo[l];
     g.out = p.x;
@@ -239,7 +260,10 @@ dlm_status run_layers(const dlm_model* m, const dlm_kv* kv, const int32_t* token
     g.K = d;
     g.lda = d;
     g.ldc = c.d_ffn;
-    DLM_TRY(gemm(g, EPI_SWIGLU, s), "gemm gate/up");
+    {
+      TimerScope t(DLM_TIMER_GATE_UP, s, l == 0);
+      DLM_TRY(gemm(g, EPI_SWIGLU, s), "gemm gate/up");
+    }
     g.a = p.u;
     g.w = m->wdown[l];
     g.out = p.x;
@@ -247,14 +271,18 @@ dlm_status run_layers(const dlm_model* m, const dlm_kv* kv, const int32_t* token
     g.K = c.d_ffn;
     g.lda = c.d_ffn;
     g.ldc = d;
-    DLM_TRY(gemm(g, EPI_RESID_F32, s), "gemm down");
+    {
+      TimerScope t(DLM_TIMER_DOWN, s, l == 0);
+      DLM_TRY(gemm(g, EPI_RESID_F32, s), "gemm down");
+    }
   }
   return DLM_OK;
 }
 
 // Final norm of the selected rows (all R if rows == null) and the fused head.
 dlm_status run_head(const dlm_model* m, int R, const int* rows, const int* count, const int* out_rows, float* conf,
-                    int32_t* argmax, float* logits, int32_t* flags, const PassBufs& p, hipStream_t s) {
+                    int32_t* argmax, float* logits, int32_t* flags, const PassBufs& p, hipStream_t s,
+                    bool time_head) {
   const dlm_config& c = m->c;
   DLM_TRY(rmsnorm(p.x, R, c.d_model, m->final_norm, c.rms_eps, p.xn, rows, count, s), "final norm");
   GemmArgs g{};
@@ -270,7 +298,10 @@ dlm_status run_head(const dlm_model* m, int R, const int* rows, const int* count
   g.logit_rows = out_rows;
   g.mask_id = c.mask_id;
   g.nonfinite = flags;
-  DLM_TRY(gemm(g, EPI_HEAD, s), "lm head");
+  {
+    TimerScope t(DLM_TIMER_LM_HEAD, s, time_head);
+    DLM_TRY(gemm(g, EPI_HEAD, s), "lm head");
+  }
   DLM_TRY(head_merge(p.head_part, c.vocab / gemm_head_tile_n(R), R, out_rows, count, conf, argmax, R, s),
           "head merge");
   return DLM_OK;
@@ -294,6 +325,16 @@ const char* dlm_status_string(dlm_status s) {
 }
 
 const char* dlm_last_error(void) { return g_err; }
+
+dlm_status dlm_set_kernel_timer(int32_t kernel, void* start_event, void* stop_event) {
+  g_err[0] = 0;
+  if (kernel < 0 || kernel >= DLM_TIMER_COUNT) return fail(DLM_ERR_INVALID_ARG, "unknown timer kernel %d", kernel);
+  if ((start_event == nullptr) != (stop_event == nullptr))
+    return fail(DLM_ERR_INVALID_ARG, "start and stop events must both be given or both NULL");
+  g_timer[kernel][0] = static_cast<hipEvent_t>(start_event);
+  g_timer[kernel][1] = static_cast<hipEvent_t>(stop_event);
+  return DLM_OK;
+}
 
 dlm_status dlm_model_create(const dlm_config* cfg, const dlm_weights* w, dlm_model** out) {
   g_err[0] = 0;
@@ -435,7 +476,7 @@ dlm_status dlm_denoise_step(const dlm_model* m, const dlm_kv* kv, const int32_t*
   const PassBufs p = carve(m->c, reinterpret_cast<uintptr_t>(ws), R, B, L, max_kv, false);
   if ((st = run_layers(m, kv, canvas, L, B, L, prefix_len, 0, 0, max_kv, flags, p, s)) != DLM_OK) return st;
   DLM_TRY(masked_rows(masked, R, p.rows, p.count, s), "masked rows");
-  return run_head(m, R, p.rows, p.count, p.rows, conf, argmax, logits, flags, p, s);
+  return run_head(m, R, p.rows, p.count, p.rows, conf, argmax, logits, flags, p, s, true);
 }
 
 dlm_status dlm_commit(const float* conf, const int32_t* argmax, int32_t* canvas, uint8_t* masked, int32_t B,
@@ -470,7 +511,7 @@ dlm_status dlm_append_block(const dlm_model* m, const dlm_kv* kv, int32_t* prefi
   const PassBufs p = carve(m->c, reinterpret_cast<uintptr_t>(ws), R, B, L, max_kv, false);
   if ((st = run_layers(m, kv, block, L, B, L, prefix_len, 0, 1, max_kv, flags, p, s)) != DLM_OK) return st;
   if (argmax_out) {
-    if ((st = run_head(m, R, nullptr, nullptr, nullptr, conf_out, argmax_out, nullptr, flags, p, s)) != DLM_OK)
+    if ((st = run_head(m, R, nullptr, nullptr, nullptr, conf_out, argmax_out, nullptr, flags, p, s, false)) != DLM_OK)
       return st;
   }
   DLM_TRY(set_prefix(prefix_len, B, 1, L, s), "advance prefix");
