@@ -92,8 +92,6 @@ struct PassBufs {
   float2* tab;
   float* part_o;
   float* part_ml;
-  float* splitk;
-  int* splitk_cnt;
   int* rows;
   int* count;
   float4* head_part;
@@ -101,19 +99,6 @@ struct PassBufs {
 };
 
 int qkv_dim(const dlm_config& c) { return (c.n_heads + 2 * c.n_kv_heads) * c.head_dim; }
-
-size_t model_splitk_floats(const dlm_config& c, int R) {
-  size_t s = 0;
-  s = std::max(s, gemm_splitk_ws_floats(R, qkv_dim(c), c.d_model));
-  s = std::max(s, gemm_splitk_ws_floats(R, c.d_model, c.n_heads * c.head_dim));
-  s = std::max(s, gemm_splitk_ws_floats(R, 2 * c.d_ffn, c.d_model));
-  s = std::max(s, gemm_splitk_ws_floats(R, c.d_model, c.d_ffn));
-  return s;
-}
-
-int model_max_n(const dlm_config& c) {
-  return std::max(std::max(qkv_dim(c), c.d_model), std::max(2 * c.d_ffn, c.vocab));
-}
 
 // attention partial floats: exact for (B, Lq, max_kv), or a bound over every
 // split of R rows into batch x tokens when B == 0.
@@ -155,11 +140,6 @@ PassBufs carve(const dlm_config& c, uintptr_t base, int R, int B, int Lq, int ma
   const size_t per = static_cast<size_t>(c.head_dim + 2);
   p.part_o = cv.take<float>(af / per * c.head_dim);
   p.part_ml = cv.take<float>(af / per * 2);
-  size_t sk = model_splitk_floats(c, R);
-  if (bound)
-    for (int r : {16, 32, 64}) sk = std::max(sk, model_splitk_floats(c, std::min(R, r)));
-  p.splitk = cv.take<float>(sk);
-  p.splitk_cnt = cv.take<int>(model_max_n(c) / 64 + 1);
   p.rows = cv.take<int>(R);
   p.count = cv.take<int>(1);
   p.head_part = cv.take<float4>(head_part_records(c, R, bound));
@@ -194,7 +174,6 @@ dlm_status run_layers(const dlm_model* m, const dlm_kv* kv, const int32_t* token
   const dlm_config& c = m->c;
   const int R = B * Lq;
   const int d = c.d_model, qd = c.n_heads * c.head_dim, nq = qkv_dim(c);
-  DLM_TRY(fill_i32(p.splitk_cnt, model_max_n(c) / 64 + 1, 0, s), "fill");
   DLM_TRY(embed_norm(tokens, R, Lq, tok_ld, m->embed, c.vocab, d, m->attn_norm[0], c.rms_eps, p.x, p.xn,
                      flags ? flags + 1 : nullptr, s),
           "embed_norm");
@@ -205,8 +184,6 @@ dlm_status run_layers(const dlm_model* m, const dlm_kv* kv, const int32_t* token
     bf16_t* vc = static_cast<bf16_t*>(kv->v) + l * lkv;
     if (l > 0) DLM_TRY(rmsnorm(p.x, R, d, m->attn_norm[l], c.rms_eps, p.xn, nullptr, nullptr, s), "rmsnorm");
     GemmArgs g{};
-    g.splitk_ws = p.splitk;
-    g.splitk_cnt = p.splitk_cnt;
     g.a = p.xn;
     g.w = m->wqkv[l];
     g.out = p.qkv;
@@ -521,8 +498,10 @@ dlm_status dlm_append_block(const dlm_model* m, const dlm_kv* kv, int32_t* prefi
 // ------------------------------------------------------------ ops ----
 
 size_t dlm_op_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K) {
-  if (M < 1 || N < 1 || K < 1) return 0;
-  return align256(gemm_splitk_ws_floats(M, N, K) * sizeof(float)) + align256((N / 64 + 1) * sizeof(int));
+  (void)M;
+  (void)N;
+  (void)K;
+  return 0;
 }
 
 dlm_status dlm_op_gemm(const void* a, const void* w, void* out, int32_t M, int32_t N, int32_t K, int32_t lda,
@@ -535,8 +514,8 @@ dlm_status dlm_op_gemm(const void* a, const void* w, void* out, int32_t M, int32
   if (epilogue < 0 || epilogue > 2) return fail(DLM_ERR_INVALID_ARG, "epilogue %d", epilogue);
   const int cols = epilogue == DLM_EPI_SWIGLU ? N / 2 : N;
   if (ldc < cols || ldc % 8) return fail(DLM_ERR_SHAPE, "ldc %d", ldc);
-  dlm_status st = check_ws(ws, ws_bytes, dlm_op_gemm_workspace_bytes(M, N, K));
-  if (st != DLM_OK) return st;
+  (void)ws;
+  (void)ws_bytes;
   hipStream_t s = static_cast<hipStream_t>(stream);
   GemmArgs g{};
   g.a = a;
@@ -547,9 +526,6 @@ dlm_status dlm_op_gemm(const void* a, const void* w, void* out, int32_t M, int32
   g.K = K;
   g.lda = lda;
   g.ldc = ldc;
-  g.splitk_ws = static_cast<float*>(ws);
-  g.splitk_cnt = reinterpret_cast<int*>(static_cast<char*>(ws) + align256(gemm_splitk_ws_floats(M, N, K) * sizeof(float)));
-  DLM_TRY(fill_i32(g.splitk_cnt, N / 64 + 1, 0, s), "fill");
   DLM_TRY(gemm(g, static_cast<GemmEpilogue>(epilogue), s), "gemm");
   return DLM_OK;
 }

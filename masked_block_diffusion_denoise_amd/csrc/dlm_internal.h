@@ -32,12 +32,8 @@ struct GemmArgs {
   const int* logit_rows; // optional: logits of result row m go to row logit_rows[m]
   int mask_id;
   int* nonfinite;       // device counter, incremented on non-finite logits
-  // split-K scratch (skinny path)
-  float* splitk_ws;     // fp32 [ks][M][N]
-  int* splitk_cnt;      // int [N / 64], zero on entry, left zero on exit
 };
 
-size_t gemm_splitk_ws_floats(int M, int N, int K);  // fp32 elements of split-K scratch
 int gemm_head_tile_n(int M);                       // vocab columns per EPI_HEAD partial
 hipError_t gemm(const GemmArgs& g, GemmEpilogue epi, hipStream_t s);
 

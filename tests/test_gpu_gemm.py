@@ -15,7 +15,10 @@ from masked_block_diffusion_denoise_amd import _lib as L
 pytestmark = pytest.mark.gpu
 
 SHAPES = [(16, 256, 128), (13, 1024, 512), (32, 6144, 4096), (64, 384, 256), (32, 4096, 14336),
-          (128, 256, 128), (200, 384, 512), (1024, 512, 4096), (96, 1024, 1024)]
+          (128, 256, 128), (200, 384, 512), (1024, 512, 4096), (96, 1024, 1024),
+          # the tiny model's projections (K parts of one or no 32-deep step per wavefront)
+          (32, 256, 128), (32, 128, 128), (32, 128, 512), (64, 256, 128), (48, 128, 512), (2, 1024, 128),
+          (80, 256, 128)]
 
 
 def operands(M, N, K, seed):
@@ -57,7 +60,7 @@ def test_gemm_residual_f32(M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(16, 1024, 128), (32, 28672, 4096), (40, 512, 256), (160, 1024, 512),
-                                   (1024, 2048, 4096)])
+                                   (1024, 2048, 4096), (32, 1024, 128), (64, 1024, 128), (80, 1024, 128)])
 def test_gemm_swiglu(M, N, K):
     announce(f"gemm swiglu {M}x{N}x{K}")
     a, w = operands(M, N, K, 3)
