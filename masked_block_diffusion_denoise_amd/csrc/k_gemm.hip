@@ -233,7 +233,10 @@ __global__ void __launch_bounds__(WAVES * 64) k_gemm_skinny(GemmArgs g) {
 // share a weight tile share that XCD's L2.
 constexpr int TL_BK = 64;
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * TL_BK + ((chunk ^ (row & 7)) << 3); }
+// 128-byte rows of 8 chunks; the LDS serves 16 lanes (256 bytes) per cycle, so
+// the XOR key changes every second row: the 16 rows read by one quarter of an
+// MFMA operand load land in 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz(int row, int chunk) { return row * TL_BK + ((chunk ^ ((row >> 1) & 7)) << 3); }
 
 template <int EPI, int BN, int BM, int WN, int WM>
 __global__ void __launch_bounds__(WN * WM * 64) k_gemm_tiled(GemmArgs g) {
@@ -267,7 +270,11 @@ __global__ void __launch_bounds__(WN * WM * 64) k_gemm_tiled(GemmArgs g) {
       src[i] = A + static_cast<size_t>(m) * g.lda + lc * 8;
     }
   }
+  // Register staging: the next stage is loaded from memory while the current
+  // one is multiplied out of LDS, then stored to the other LDS buffer.
   u32x4 st[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) st[i] = u32x4{0, 0, 0, 0};
   auto gload = [&](int kt) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) st[i] = ld16(src[i] + kt * TL_BK);
@@ -295,16 +302,16 @@ __global__ void __launch_bounds__(WN * WM * 64) k_gemm_tiled(GemmArgs g) {
     if (kt + 1 < nk) gload(kt + 1);
 #pragma unroll
     for (int s = 0; s < TL_BK / 16; ++s) {
-      bf16x8 a[TN], b[TM];
+      bf16x8 fa[TN], fb[TM];
 #pragma unroll
-      for (int i = 0; i < TN; ++i) a[i] = as_bf16x8(ld16(&lds[buf][swz(wn * TN * 32 + i * 32 + arow, 2 * s + ahalf)]));
+      for (int i = 0; i < TN; ++i) fa[i] = as_bf16x8(ld16(&lds[buf][swz(wn * TN * 32 + i * 32 + arow, 2 * s + ahalf)]));
 #pragma unroll
       for (int j = 0; j < TM; ++j)
-        b[j] = as_bf16x8(ld16(&lds[buf][swz(BN + wm * TM * 32 + j * 32 + arow, 2 * s + ahalf)]));
+        fb[j] = as_bf16x8(ld16(&lds[buf][swz(BN + wm * TM * 32 + j * 32 + arow, 2 * s + ahalf)]));
 #pragma unroll
       for (int i = 0; i < TN; ++i)
 #pragma unroll
-        for (int j = 0; j < TM; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < TM; ++j) acc[i][j] = mfma32x32x16(fa[i], fb[j], acc[i][j]);
     }
     if (kt + 1 < nk) lstore(buf ^ 1);
     __syncthreads();
@@ -421,7 +428,9 @@ static hipError_t launch_epi(const GemmArgs& g, hipStream_t s) {
     else
       launch_skinny<4, EPI>(g, s);
   } else {
-    if constexpr (EPI == EPI_HEAD)
+    // 256 x 256 tiles where they still give at least one wave of workgroups
+    // (the LM head, the SwiGLU gate/up projection); 128 x 128 otherwise
+    if (EPI == EPI_HEAD || (g.N / 256) * ((g.M + 255) / 256) >= 256)
       launch_tiled<EPI, 256, 256, 4, 2>(g, s);
     else
       launch_tiled<EPI, 128, 128, 2, 2>(g, s);
