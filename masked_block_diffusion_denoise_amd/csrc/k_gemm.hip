@@ -83,7 +83,7 @@ __global__ void __launch_bounds__(WAVES * 64) k_gemm_skinny(GemmArgs g) {
   constexpr int KP = WAVES / NG;
   __shared__ float red[WAVES * MT * 4 * 64];
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rg = w % NG, kp = w / NG;
   const int tile = blockIdx.x;
   const int n_w = (tile * NG + rg) * 16;
@@ -115,13 +115,14 @@ __global__ void __launch_bounds__(WAVES * 64) k_gemm_skinny(GemmArgs g) {
 #pragma unroll
     for (int t = 0; t < MT; ++t) xa[u][t] = xb[u][t] = u32x4{0, 0, 0, 0};
   }
+  // Loads are unconditional (steps past the end reload the last step, which is
+  // in bounds and never multiplied) so that the wait before each batch's MFMAs
+  // only covers that batch and the next batch stays in flight.
 #define SK_LOAD(WV, XV, S0)                                              \
   _Pragma("unroll") for (int u = 0; u < SK_U; ++u) {                     \
-    const int st = (S0) + u;                                             \
-    if (st < s_end) {                                                    \
-      WV[u] = ld16(wp + st * 32);                                        \
-      _Pragma("unroll") for (int t = 0; t < MT; ++t) XV[u][t] = ld16(ap[t] + st * 32); \
-    }                                                                    \
+    const int st = min((S0) + u, s_last);                                \
+    WV[u] = ld16(wp + st * 32);                                          \
+    _Pragma("unroll") for (int t = 0; t < MT; ++t) XV[u][t] = ld16(ap[t] + st * 32); \
   }
 #define SK_COMP(WV, XV, S0)                                              \
   _Pragma("unroll") for (int u = 0; u < SK_U; ++u) {                     \
@@ -130,7 +131,8 @@ __global__ void __launch_bounds__(WAVES * 64) k_gemm_skinny(GemmArgs g) {
         acc[t] = mfma16x16x32(as_bf16x8(WV[u]), as_bf16x8(XV[u][t]), acc[t]); \
     }                                                                    \
   }
-  SK_LOAD(wa, xa, s_begin);
+  const int s_last = max(s_end - 1, 0);
+  if (s_begin < s_end) SK_LOAD(wa, xa, s_begin);
   for (int s = s_begin; s < s_end; s += 2 * SK_U) {
     SK_LOAD(wb, xb, s + SK_U);
     SK_COMP(wa, xa, s);
