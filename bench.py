@@ -17,6 +17,7 @@ import argparse
 import ctypes as C
 import hashlib
 import json
+import re
 import os
 import sys
 import time
@@ -24,10 +25,9 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+from masked_block_diffusion_denoise_amd import roofline as RL  # noqa: E402
+
 METRIC = "committed tokens/s & denoise steps/s, 8B-class bf16 b=1/32; % HBM/MFMA roofline"
-HBM_PEAK_GBS = 8000.0
-MFMA_BF16_PEAK_TFLOPS = 2500.0
-RIDGE = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
 
 
 class HipEvents:
@@ -60,41 +60,9 @@ class HipEvents:
         self.events = []
 
 
-def kernel_work(name, B, Lb, P, masked_rows, shape):
-    """Algorithmic bytes and flops of one launch (what the method must move/compute)."""
-    d, H, G, hd, F, V = (shape.d_model, shape.n_heads, shape.n_kv_heads, shape.head_dim, shape.d_ffn,
-                         shape.vocab)
-    M = B * Lb
-    if name == "lm_head":
-        return V * d * 2 + masked_rows * d * 2, 2.0 * masked_rows * d * V
-    if name == "attention":
-        kv = P + Lb
-        return B * kv * G * hd * 2 * 2 + M * H * hd * 2 * 2, 4.0 * B * Lb * H * hd * kv
-    if name == "gate_up":
-        return 2 * F * d * 2 + M * d * 2 + M * F * 2, 2.0 * M * d * 2 * F
-    if name == "down":
-        return d * F * 2 + M * F * 2 + M * d * 4 * 2, 2.0 * M * F * d
-    if name == "qkv":
-        n = (H + 2 * G) * hd
-        return n * d * 2 + M * d * 2 + M * n * 2, 2.0 * M * d * n
-    raise KeyError(name)
-
-
-def roofline(bytes_, flops, ms, traffic=None):
-    s = ms * 1e-3
-    ai = flops / bytes_
-    if ai >= RIDGE:
-        a = flops / s / 1e12
-        return {"bound": "mfma", "achieved": round(a, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(a / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic}
-    a = bytes_ / s / 1e9
-    return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(a / HBM_PEAK_GBS, 4), "traffic": traffic}
-
-
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("k_gemm.hip", "dlm_device.h"):
+    for f in ("k_gemm.hip", "dlm_device.h", "dlm_internal.h"):
         h.update(open(os.path.join(ROOT, "masked_block_diffusion_denoise_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -114,6 +82,60 @@ def traffic_for(kernel: str, batch: int):
 
 
 TIMERS = {"lm_head": 0, "attention": 1, "gate_up": 2, "down": 3, "qkv": 4}
+
+# LM-head launches in a counter run: the tiled kernel (batch 32) and the skinny
+# one (batch 1), told apart from the other GEMMs by the head epilogue's template
+# argument (k_gemm_tiled<EPI, ...>, k_gemm_skinny<MT, EPI, ...>; EPI_HEAD = 3).
+HEAD_KERNELS = {"lm_head_b32": re.compile(r"k_gemm_tiled<3,"), "lm_head_b1": re.compile(r"k_gemm_skinny<\d+, 3,")}
+COPY_KERNEL = re.compile(r"copyBuffer")
+
+
+def copy_probe(mib: int) -> None:
+    """A plain device-to-device copy of `mib` MiB, run three times before the steps
+    so that a counter run sees a kernel whose HBM bytes are known."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def _counter_means(d: str, counter: str) -> dict:
+    """Mean per-dispatch value of `counter` for each kernel name in a rocprofv3 csv directory."""
+    import csv
+    import glob
+    vals: dict = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for row in csv.DictReader(open(f)):
+            if row["Counter_Name"] != counter:
+                continue
+            vals.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return vals
+
+
+def traffic_from(fetch_dir: str, write_dir: str, copy_mib: int, command: str) -> dict:
+    """Per-launch HBM bytes of the LM head from a FETCH_SIZE run and a WRITE_SIZE run,
+    each scaled by what the counter read for the copy probe (known bytes / counter bytes)."""
+    out = {"source_hash": kernel_source_hash(), "command": command, "copy_probe_bytes": copy_mib << 20,
+           "per_launch_bytes": {}, "raw_kib": {}}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        vals = _counter_means(d, counter)
+        copies = [max(v) for k, v in vals.items() if COPY_KERNEL.search(k)]
+        if not copies:
+            raise SystemExit(f"no copy dispatch with {counter} in {d}")
+        scale = (copy_mib << 20) / (max(copies) * 1024.0)
+        out[f"{counter.lower()}_scale"] = round(scale, 4)
+        for key, pat in HEAD_KERNELS.items():
+            launches = [x for k, v in vals.items() if pat.search(k) for x in v]
+            if not launches:
+                continue
+            kib = sum(launches) / len(launches)
+            out["raw_kib"][f"{key}_{counter}"] = round(kib, 1)
+            out["per_launch_bytes"][key] = out["per_launch_bytes"].get(key, 0) + round(kib * 1024.0 * scale)
+    return out
 
 
 def run_batch(model, shape, B, steps, warmup, P=4096, Lb=32, seed=3):
@@ -168,16 +190,17 @@ def run_batch(model, shape, B, steps, warmup, P=4096, Lb=32, seed=3):
     mrows = int(masked.sum())
     kernels = {}
     for n, t in kms.items():
-        by, fl = kernel_work(n, B, Lb, P, mrows, shape)
+        by, fl = RL.kernel_work(n, B, Lb, P, mrows, shape.d_model, shape.n_heads, shape.n_kv_heads,
+                                shape.head_dim, shape.d_ffn, shape.vocab)
         kernels[n] = {"ms": round(t, 4), "bytes": by, "flops": fl,
-                      "roofline": roofline(by, fl, t, traffic_for(n, B))}
+                      "roofline": RL.roofline(by, fl, t, traffic_for(n, B))}
     return {"batch": B, "ms_per_step": ms_step, "steps_per_s": 1e3 / ms_step,
             "committed_per_step": committed, "committed_tokens_per_s": committed * 1e3 / ms_step,
             "masked_rows": mrows, "kernels": kernels, "flags": flags,
             "inputs": (canvas, masked)}
 
 
-def cpu_baseline(w, shape, B, canvas, masked, P=4096, seed=3, rows=3):
+def cpu_baseline(w, shape, B, canvas, masked, P=4096, seed=3, rows=16):
     """The oracle (float64 NumPy) on a bounded sample: `rows` batch rows of the step."""
     import numpy as np
 
@@ -211,10 +234,22 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--batches", default="32,1", help="batch sizes; the first is the headline")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run a plain copy of this many MiB first (scale for counter runs)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU: digest two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
+                         "`bench.py --copy-probe-mib N` into profiles/lm_head_traffic.json")
+    ap.add_argument("--traffic-command", default="", help="the counter command, recorded with --traffic-from")
     a = ap.parse_args(argv)
+    if a.traffic_from:
+        rec = traffic_from(a.traffic_from[0], a.traffic_from[1], a.copy_probe_mib or 1024, a.traffic_command)
+        with open(os.path.join(ROOT, "profiles", "lm_head_traffic.json"), "w") as f:
+            json.dump(rec, f, indent=1)
+        print(json.dumps(rec))
+        return 0
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (rows shard by data "
-              "parallelism with no exchange; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: libdlm has no multi-GPU path (batch rows would shard across "
+              "GPUs by data parallelism with no exchange). Run with --gpus 1.", file=sys.stderr)
         return 2
     import numpy as np
     import torch
@@ -224,6 +259,8 @@ def main(argv=None) -> int:
     import synth
     from masked_block_diffusion_denoise_amd import runtime as R
 
+    if a.copy_probe_mib:
+        copy_probe(a.copy_probe_mib)
     shape = synth.LAYER_8B
     print(f"[bench] generating weights", file=sys.stderr, flush=True)
     w = synth.model_weights(shape, seed=0)

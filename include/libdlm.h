@@ -49,7 +49,7 @@ typedef enum {
   DLM_ERR_INVALID_ARG = -1, /* null / misaligned pointer, non-finite or out-of-range scalar */
   DLM_ERR_SHAPE = -2,       /* sizes inconsistent with each other or with the model */
   DLM_ERR_CAPACITY = -3,    /* KV cache too small for the positions written */
-  DLM_ERR_UNSUPPORTED = -4, /* a shape this build has no kernel for (e.g. head_dim not 32/128) */
+  DLM_ERR_UNSUPPORTED = -4, /* a shape the library has no kernel for (e.g. head_dim not 32/128) */
   DLM_ERR_HIP = -5,         /* a kernel launch failed (text in dlm_last_error) */
   DLM_ERR_WORKSPACE = -6    /* ws_bytes smaller than the call needs */
 } dlm_status;
