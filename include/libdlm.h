@@ -60,7 +60,7 @@ typedef enum {
  * head_dim in {32, 128}; n_heads / n_kv_heads in {1, 2, 4}; d_model,
  * n_heads*head_dim and d_ffn multiples of 256 (or 64..256 and multiples of 64);
  * (n_heads + 2*n_kv_heads)*head_dim, d_model and 2*d_ffn multiples of 128;
- * vocab a multiple of 128; 0 <= mask_id < vocab; rope_base > 0; rms_eps > 0. */
+ * vocab a multiple of 256; 0 <= mask_id < vocab; rope_base > 0; rms_eps > 0. */
 typedef struct {
   int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, d_ffn, vocab, mask_id;
   float rope_base; /* RoPE: pair (i, i+hd/2) turns by pos * rope_base^(-2i/hd) */

@@ -69,6 +69,7 @@ dlm_status dlm_op_attention(const void* q, int32_t ldq, const void* k_cache, con
  * reaching the max logit, computed per vocabulary tile and merged, without
  * writing the logits (unless logits [dev] fp32 [R][V] is given; -inf at mask_id).
  * flags [dev] int32 [2] or NULL: flags[0] += rows' tiles with non-finite logits.
+ * Requirements: V a multiple of 256; d as K of dlm_op_gemm.
  * ws: dlm_op_lm_head_workspace_bytes(R, V) bytes. */
 size_t dlm_op_lm_head_workspace_bytes(int32_t R, int32_t V);
 dlm_status dlm_op_lm_head(const void* hidden, int32_t R, int32_t d, const void* head, int32_t V, int32_t mask_id,

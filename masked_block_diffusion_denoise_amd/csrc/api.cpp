@@ -326,8 +326,8 @@ dlm_status dlm_model_create(const dlm_config* cfg, const dlm_weights* w, dlm_mod
   if (gs != 1 && gs != 2 && gs != 4) return fail(DLM_ERR_UNSUPPORTED, "query heads per KV head %d (need 1, 2 or 4)", gs);
   if (!gemm_k_ok(c.d_model) || !gemm_k_ok(static_cast<long>(c.n_heads) * c.head_dim) || !gemm_k_ok(c.d_ffn))
     return fail(DLM_ERR_UNSUPPORTED, "d_model, n_heads*head_dim and d_ffn must be multiples of 256 (or of 64 up to 256)");
-  if (qkv_dim(c) % 128 || c.d_model % 128 || (2 * c.d_ffn) % 128 || c.vocab % 128)
-    return fail(DLM_ERR_UNSUPPORTED, "(H+2G)*hd, d_model, 2*d_ffn and vocab must be multiples of 128");
+  if (qkv_dim(c) % 128 || c.d_model % 128 || (2 * c.d_ffn) % 128 || c.vocab % 256)
+    return fail(DLM_ERR_UNSUPPORTED, "(H+2G)*hd, d_model and 2*d_ffn must be multiples of 128, vocab of 256");
   if (c.mask_id < 0 || c.mask_id >= c.vocab) return fail(DLM_ERR_INVALID_ARG, "mask_id %d outside [0, %d)", c.mask_id, c.vocab);
   if (!(std::isfinite(c.rope_base) && c.rope_base > 0.f)) return fail(DLM_ERR_INVALID_ARG, "rope_base must be finite and > 0");
   if (!(std::isfinite(c.rms_eps) && c.rms_eps > 0.f)) return fail(DLM_ERR_INVALID_ARG, "rms_eps must be finite and > 0");
@@ -630,7 +630,7 @@ dlm_status dlm_op_lm_head(const void* hidden, int32_t R, int32_t d, const void* 
       !aligned4(argmax))
     return fail(DLM_ERR_INVALID_ARG, "hidden/head/conf/argmax NULL or misaligned");
   if (logits && !aligned16(logits)) return fail(DLM_ERR_INVALID_ARG, "logits must be 16-byte aligned");
-  if (R < 1 || V < 128 || V % 128 || !gemm_k_ok(d)) return fail(DLM_ERR_SHAPE, "lm head shape R=%d V=%d d=%d", R, V, d);
+  if (R < 1 || V < 256 || V % 256 || !gemm_k_ok(d)) return fail(DLM_ERR_SHAPE, "lm head shape R=%d V=%d d=%d", R, V, d);
   if (mask_id < 0 || mask_id >= V) return fail(DLM_ERR_INVALID_ARG, "mask_id %d", mask_id);
   dlm_status st = check_ws(ws, ws_bytes, dlm_op_lm_head_workspace_bytes(R, V));
   if (st != DLM_OK) return st;

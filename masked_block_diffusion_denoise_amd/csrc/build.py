@@ -51,6 +51,15 @@ def build(jobs: int = 4, verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    # a kernel whose host-side launch stub was not emitted links fine and only
+    # fails when the library is loaded: refuse such a build here
+    nm = shutil.which("nm")
+    if nm:
+        und = subprocess.run([nm, "-C", "--undefined-only", tmp], capture_output=True, text=True).stdout
+        stubs = [l.strip() for l in und.splitlines() if "__device_stub__" in l]
+        if stubs:
+            os.remove(tmp)
+            raise RuntimeError("kernel launch stubs missing from the host objects:\n" + "\n".join(stubs))
     os.replace(tmp, OUT)
     if verbose:
         print(f"built {OUT}")

@@ -6,15 +6,16 @@
 // an MFMA result holds consecutive output columns of one row and stores them as
 // one vector.
 //
-// Skinny tiling (M <= 64, one denoise canvas at batch 1-2): the weight matrix is
-// read exactly once, streamed from HBM straight into MFMA operand registers
-// (v_mfma_f32_16x16x32_bf16), K split over the wavefronts of a workgroup and
-// summed through LDS -- no cross-workgroup reduction (whose release fence would
-// write back the L2 of an XCD).
+// Skinny tiling (M <= 64, one denoise canvas at batch 1-2, layer projections):
+// the weight matrix is read exactly once, streamed from HBM straight into MFMA
+// operand registers (v_mfma_f32_16x16x32_bf16), K split over the wavefronts of a
+// workgroup and summed through LDS -- no cross-workgroup reduction (whose
+// release fence would write back the L2 of an XCD).
 //
-// Tiled (M > 64): 256 x 256 (LM head, eight wavefronts) or 128 x 128 (four)
-// output tiles, 64-deep K stages double-buffered in LDS, each wavefront a block
-// of v_mfma_f32_32x32x16_bf16 tiles.
+// Tiled (M > 64, and the LM head at any M): 256 x 256, 256 x 128, 256 x 64 or
+// 128 x 128 output tiles, 32-deep K stages in a ring of LDS buffers filled by
+// direct global-to-LDS loads, each wavefront a block of
+// v_mfma_f32_32x32x16_bf16 tiles.
 #include <algorithm>
 
 #include "dlm_device.h"
@@ -143,7 +144,7 @@ __global__ void __launch_bounds__(WAVES * 64) k_gemm_skinny(GemmArgs g) {
 #undef SK_COMP
 
   // lane holds D[n][m] for n = n_w + 4*(lane>>4) + r, m = t*16 + (lane & 15)
-  if (KP > 1 || EPI == EPI_SWIGLU || EPI == EPI_HEAD) {
+  if (KP > 1 || EPI == EPI_SWIGLU) {
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
@@ -182,70 +183,95 @@ __global__ void __launch_bounds__(WAVES * 64) k_gemm_skinny(GemmArgs g) {
         *reinterpret_cast<u32x2*>(o) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
       }
     }
-  } else if (EPI == EPI_HEAD) {
-    // every wavefront reduces its own 16 vocab rows (summing the K parts), then
-    // wavefront 0 merges the NG groups of the tile
-    __shared__ float hm[NG * MT * 16], hs[NG * MT * 16];
-    __shared__ int hi[NG * MT * 16];
-    bool bad = false;
-    if (w < NG) {
-      const int nq = n_w + 4 * (lane >> 4);
-#pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        const int m = t * 16 + (lane & 15);
-        float v[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = (KP > 1) ? summed(rg, t, r) : acc[t][r];
-        if (g.logits && m < M) {
-          float* lo = g.logits + static_cast<size_t>(g.logit_rows ? g.logit_rows[m] : m) * g.N + nq;
-          float4 o4 = make_float4(v[0], v[1], v[2], v[3]);
-          if (nq <= g.mask_id && g.mask_id < nq + 4) (&o4.x)[g.mask_id - nq] = -INFINITY;
-          *reinterpret_cast<float4*>(lo) = o4;
-        }
-        MaxSumIdx p = head_quad(v, nq, g.mask_id, bad);
-        p = msi_shfl_xor(p, 16);
-        p = msi_shfl_xor(p, 32);
-        if (lane < 16) {
-          hm[(rg * MT + t) * 16 + lane] = p.m;
-          hs[(rg * MT + t) * 16 + lane] = p.s;
-          hi[(rg * MT + t) * 16 + lane] = p.idx;
-        }
-      }
-      if (__ballot(bad) && lane == 0 && g.nonfinite) atomicAdd(g.nonfinite, 1);
-    }
-    __syncthreads();
-    if (threadIdx.x < MT * 16) {
-      const int mm = threadIdx.x;  // = t*16 + row
-      MaxSumIdx p{hm[mm], hs[mm], hi[mm]};
-      for (int q = 1; q < NG; ++q) p = msi_combine(p, MaxSumIdx{hm[q * MT * 16 + mm], hs[q * MT * 16 + mm], hi[q * MT * 16 + mm]});
-      if (mm < M)
-        reinterpret_cast<float4*>(g.partials)[static_cast<size_t>(tile) * g.M + mm] =
-            make_float4(p.m, p.s, __int_as_float(p.idx), 0.f);
-    }
   }
 }
 
 // ======================================================== tiled GEMM ====
 // BN x BM output tile (weights x activations) per workgroup of WN x WM
-// wavefronts, each a (BN/WN) x (BM/WM) block of 32 x 32 MFMA tiles; 64-deep K
-// stages double-buffered in LDS through registers; 16-byte chunks XOR-swizzled
-// by row so the 32 rows of an MFMA operand read spread over the LDS banks.
+// wavefronts, each a (BN/WN) x (BM/WM) block of 32 x 32 MFMA tiles.
+//
+// K runs in 32-deep stages through a ring of NBUF LDS buffers filled by direct
+// global-to-LDS loads (global_load_lds_dwordx4: each lane's 16 bytes land at
+// the instruction's LDS base + 16 * lane), so NBUF - 1 stages are in flight
+// while one is multiplied, without staging registers.  One wait + barrier per
+// stage: it makes the stage visible to every wavefront and retires the buffer
+// that the next load refills.  Operand fragments are read from LDS in inline
+// asm that waits for its own reads, so the compiler's conservative wait for
+// LDS DMA (it cannot tell the ring buffers apart) is never inserted.
+//
 // Tiles are ordered per XCD: workgroup i runs on XCD i % 8, so XCD x takes a
 // contiguous range of tiles, activation tiles fastest, and the workgroups that
 // share a weight tile share that XCD's L2.
-constexpr int TL_BK = 64;
+constexpr int TL_BK = 32;                 // K per stage
+constexpr int TL_ROW = TL_BK * 2;         // bytes per row of a stage (4 chunks of 16 B)
 
-// 128-byte rows of 8 chunks; the LDS serves 16 lanes (256 bytes) per cycle, so
-// the XOR key changes every second row: the 16 rows read by one quarter of an
-// MFMA operand load land in 16 distinct 16-byte bank groups.
-__device__ __forceinline__ int swz(int row, int chunk) { return row * TL_BK + ((chunk ^ ((row >> 1) & 7)) << 3); }
+// Byte offset of 16-byte chunk c (0..3) of row `row` in a stage region.  The
+// LDS serves 16 lanes (256 bytes, four 64-byte rows) per cycle; XOR-ing the
+// chunk with bits 2-3 of the row sends the 16 rows of one quarter of an MFMA
+// operand read to 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz(int row, int c) { return row * TL_ROW + ((c ^ ((row >> 2) & 3)) << 4); }
 
-template <int EPI, int BN, int BM, int WN, int WM>
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p));
+}
+
+// One 16-byte direct global-to-LDS load per lane: lane l's bytes land at
+// lds_dst + 16 l (lds_dst must be the same for the whole wavefront).
+__device__ __forceinline__ void load_lds16(const void* src, void* lds_dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
+}
+
+// Wait until at most N of this wavefront's vector-memory operations are
+// outstanding, then join the workgroup barrier.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"i"(N) : "memory");
+}
+
+// Fragment reads of one 16-deep step: TN weight fragments at a + 2048 i and TM
+// activation fragments at b + 2048 j (consecutive 32-row blocks), each one
+// ds_read_b128 per lane; the asm waits for its reads before returning.
+template <int TN, int TM>
+__device__ __forceinline__ void lds_frags(uint32_t a, uint32_t b, u32x4 (&fa)[TN], u32x4 (&fb)[TM]);
+
+template <>
+__device__ __forceinline__ void lds_frags<2, 4>(uint32_t a, uint32_t b, u32x4 (&fa)[2], u32x4 (&fb)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %6\n\t"
+      "ds_read_b128 %1, %6 offset:2048\n\t"
+      "ds_read_b128 %2, %7\n\t"
+      "ds_read_b128 %3, %7 offset:2048\n\t"
+      "ds_read_b128 %4, %7 offset:4096\n\t"
+      "ds_read_b128 %5, %7 offset:6144\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(fa[0]), "=&v"(fa[1]), "=&v"(fb[0]), "=&v"(fb[1]), "=&v"(fb[2]), "=&v"(fb[3])
+      : "v"(a), "v"(b)
+      : "memory");
+}
+
+template <>
+__device__ __forceinline__ void lds_frags<2, 2>(uint32_t a, uint32_t b, u32x4 (&fa)[2], u32x4 (&fb)[2]) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %4 offset:2048\n\t"
+      "ds_read_b128 %2, %5\n\t"
+      "ds_read_b128 %3, %5 offset:2048\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(fa[0]), "=&v"(fa[1]), "=&v"(fb[0]), "=&v"(fb[1])
+      : "v"(a), "v"(b)
+      : "memory");
+}
+
+template <int EPI, int BN, int BM, int WN, int WM, int NBUF>
 __global__ void __launch_bounds__(WN * WM * 64) k_gemm_tiled(GemmArgs g) {
   constexpr int T = WN * WM * 64;
   constexpr int TN = BN / WN / 32, TM = BM / WM / 32;
-  constexpr int CPT = (BN + BM) * 8 / T;  // 16-byte chunks per thread per stage
-  __shared__ __attribute__((aligned(16))) bf16_t lds[2][(BN + BM) * TL_BK];
+  constexpr int STAGE = (BN + BM) * TL_ROW;       // bytes per stage
+  constexpr int BLK = STAGE / 1024 / (T / 64);    // 1-KB load blocks per wavefront per stage
+  static_assert(STAGE % (1024 * (T / 64)) == 0, "stage must split into 1 KB blocks per wavefront");
+  static_assert(BN % 16 == 0, "a 1 KB block (16 rows) must not straddle the weight/activation regions");
+  static_assert(NBUF >= 2 && NBUF <= 6, "wait ladder covers up to four later stages");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NBUF * STAGE];
 
   const int nN = g.N / BN, nM = (g.M + BM - 1) / BM;
   const int total = nN * nM, per = (total + 7) / 8;
@@ -255,35 +281,32 @@ __global__ void __launch_bounds__(WN * WM * 64) k_gemm_tiled(GemmArgs g) {
   const int M = g.m_dev ? min(g.M, *g.m_dev) : g.M;
   if (m0 >= M) return;
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wn = w % WN, wm = w / WN;
   const bf16_t* A = static_cast<const bf16_t*>(g.a);
   const bf16_t* W = static_cast<const bf16_t*>(g.w);
 
-  const int lc = threadIdx.x & 7, lr = threadIdx.x >> 3;  // chunk column, first row
-  const bf16_t* src[CPT];
+  // Load block q = w*BLK + b of a stage is 16 rows x 64 bytes; lane l fills the
+  // 16-byte slot 64q + l, i.e. physical chunk l % 4 of row 16q' + l / 4 of its
+  // region, and so reads the logical chunk that the swizzle puts there.
+  const bf16_t* src[BLK];
 #pragma unroll
-  for (int i = 0; i < CPT; ++i) {
-    const int row = lr + i * (T / 8);
+  for (int b = 0; b < BLK; ++b) {
+    const int slot = (w * BLK + b) * 64 + lane;
+    const int row = slot >> 2;
+    const int c = (slot & 3) ^ ((row >> 2) & 3);
     if (row < BN) {
-      src[i] = W + static_cast<size_t>(n0 + row) * g.K + lc * 8;
+      src[b] = W + static_cast<size_t>(n0 + row) * g.K + c * 8;
     } else {
       const int m = min(m0 + row - BN, M - 1);  // rows past M repeat the last row; discarded
-      src[i] = A + static_cast<size_t>(m) * g.lda + lc * 8;
+      src[b] = A + static_cast<size_t>(m) * g.lda + c * 8;
     }
   }
-  // Register staging: the next stage is loaded from memory while the current
-  // one is multiplied out of LDS, then stored to the other LDS buffer.
-  u32x4 st[CPT];
+  auto issue = [&](int kt) {
+    uint8_t* dst = lds + (kt % NBUF) * STAGE + w * BLK * 1024;
 #pragma unroll
-  for (int i = 0; i < CPT; ++i) st[i] = u32x4{0, 0, 0, 0};
-  auto gload = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) st[i] = ld16(src[i] + kt * TL_BK);
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) st16(&lds[buf][swz(lr + i * (T / 8), lc)], st[i]);
+    for (int b = 0; b < BLK; ++b)
+      load_lds16(src[b] + kt * TL_BK, dst + b * 1024);
   };
 
   f32x16 acc[TN][TM];
@@ -296,27 +319,42 @@ __global__ void __launch_bounds__(WN * WM * 64) k_gemm_tiled(GemmArgs g) {
 
   const int nk = g.K / TL_BK;
   const int arow = lane & 31, ahalf = lane >> 5;
-  gload(0);
-  lstore(0);
-  __syncthreads();
+  // fragment offsets within a stage for the two 16-deep steps (chunk 2s + ahalf)
+  uint32_t fa_off[2], fb_off[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    fa_off[s] = swz(wn * TN * 32 + arow, 2 * s + ahalf);
+    fb_off[s] = BN * TL_ROW + swz(wm * TM * 32 + arow, 2 * s + ahalf);
+  }
+  const uint32_t lbase = lds_addr(lds);
+
+#pragma unroll
+  for (int p = 0; p < NBUF - 1; ++p)
+    if (p < nk) issue(p);
   for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
+    // stage kt has landed once at most the later stages' loads are outstanding
+    const int later = min(nk - 1 - kt, NBUF - 2);
+    if (later >= 4)
+      wait_vm_barrier<4 * BLK>();
+    else if (later == 3)
+      wait_vm_barrier<3 * BLK>();
+    else if (later == 2)
+      wait_vm_barrier<2 * BLK>();
+    else if (later == 1)
+      wait_vm_barrier<BLK>();
+    else
+      wait_vm_barrier<0>();
+    if (kt + NBUF - 1 < nk) issue(kt + NBUF - 1);
+    const uint32_t sb = lbase + (kt % NBUF) * STAGE;
 #pragma unroll
-    for (int s = 0; s < TL_BK / 16; ++s) {
-      bf16x8 fa[TN], fb[TM];
-#pragma unroll
-      for (int i = 0; i < TN; ++i) fa[i] = as_bf16x8(ld16(&lds[buf][swz(wn * TN * 32 + i * 32 + arow, 2 * s + ahalf)]));
-#pragma unroll
-      for (int j = 0; j < TM; ++j)
-        fb[j] = as_bf16x8(ld16(&lds[buf][swz(BN + wm * TM * 32 + j * 32 + arow, 2 * s + ahalf)]));
+    for (int s = 0; s < 2; ++s) {
+      u32x4 fa[TN], fb[TM];
+      lds_frags<TN, TM>(sb + fa_off[s], sb + fb_off[s], fa, fb);
 #pragma unroll
       for (int i = 0; i < TN; ++i)
 #pragma unroll
-        for (int j = 0; j < TM; ++j) acc[i][j] = mfma32x32x16(fa[i], fb[j], acc[i][j]);
+        for (int j = 0; j < TM; ++j) acc[i][j] = mfma32x32x16(as_bf16x8(fa[i]), as_bf16x8(fb[j]), acc[i][j]);
     }
-    if (kt + 1 < nk) lstore(buf ^ 1);
-    __syncthreads();
   }
 
   // lane holds D[n][m]: m = m0 + (wm*TM + j)*32 + (lane&31),
@@ -397,21 +435,19 @@ __global__ void __launch_bounds__(WN * WM * 64) k_gemm_tiled(GemmArgs g) {
 }
 
 // ============================================================== host ====
-// LM-head vocabulary columns per partial record: 64 (skinny) or 256 (tiled).
-int gemm_head_tile_n(int M) { return M <= 64 ? 64 : 256; }
+// LM-head vocabulary columns per partial record (the tiled kernels' BN).
+int gemm_head_tile_n(int) { return 256; }
 
-template <int EPI, int BN, int BM, int WN, int WM>
+template <int EPI, int BN, int BM, int WN, int WM, int NBUF>
 static void launch_tiled(const GemmArgs& g, hipStream_t s) {
   const int total = (g.N / BN) * ((g.M + BM - 1) / BM);
   const int per = (total + 7) / 8;
-  hipLaunchKernelGGL((k_gemm_tiled<EPI, BN, BM, WN, WM>), dim3(8 * per), dim3(WN * WM * 64), 0, s, g);
+  hipLaunchKernelGGL((k_gemm_tiled<EPI, BN, BM, WN, WM, NBUF>), dim3(8 * per), dim3(WN * WM * 64), 0, s, g);
 }
 
 template <int MT, int EPI>
 static void launch_skinny(const GemmArgs& g, hipStream_t s) {
-  if constexpr (EPI == EPI_HEAD) {
-    hipLaunchKernelGGL((k_gemm_skinny<MT, EPI, 4, 4>), dim3(g.N / 64), dim3(256), 0, s, g);
-  } else if constexpr (EPI == EPI_SWIGLU) {
+  if constexpr (EPI == EPI_SWIGLU) {
     hipLaunchKernelGGL((k_gemm_skinny<MT, EPI, 2, 4>), dim3(g.N / 32), dim3(256), 0, s, g);
   } else if (g.N / 16 < 512) {
     hipLaunchKernelGGL((k_gemm_skinny<MT, EPI, 1, 8>), dim3(g.N / 16), dim3(512), 0, s, g);
@@ -422,7 +458,17 @@ static void launch_skinny(const GemmArgs& g, hipStream_t s) {
 
 template <int EPI>
 static hipError_t launch_epi(const GemmArgs& g, hipStream_t s) {
-  if (g.M <= 64) {
+  if constexpr (EPI == EPI_HEAD) {
+    // The head streams 1 GB of weights: at up to 128 scored rows it is HBM-bound,
+    // and short tiles whose activation rows every wavefront shares from LDS, two
+    // workgroups per CU, keep the most bytes in flight; 256 x 256 tiles otherwise.
+    if (g.M <= 64)
+      launch_tiled<EPI, 256, 64, 4, 1, 3>(g, s);
+    else if (g.M <= 128)
+      launch_tiled<EPI, 256, 128, 4, 2, 3>(g, s);
+    else
+      launch_tiled<EPI, 256, 256, 4, 2, 4>(g, s);
+  } else if (g.M <= 64) {
     if (g.M <= 16)
       launch_skinny<1, EPI>(g, s);
     else if (g.M <= 32)
@@ -431,11 +477,11 @@ static hipError_t launch_epi(const GemmArgs& g, hipStream_t s) {
       launch_skinny<4, EPI>(g, s);
   } else {
     // 256 x 256 tiles where they still give at least one wave of workgroups
-    // (the LM head, the SwiGLU gate/up projection); 128 x 128 otherwise
-    if (EPI == EPI_HEAD || (g.N / 256) * ((g.M + 255) / 256) >= 256)
-      launch_tiled<EPI, 256, 256, 4, 2>(g, s);
+    // (the SwiGLU gate/up projection); 128 x 128 otherwise
+    if (g.N % 256 == 0 && (g.N / 256) * ((g.M + 255) / 256) >= 256)
+      launch_tiled<EPI, 256, 256, 4, 2, 4>(g, s);
     else
-      launch_tiled<EPI, 128, 128, 2, 2>(g, s);
+      launch_tiled<EPI, 128, 128, 2, 2, 4>(g, s);
   }
   return hipGetLastError();
 }

@@ -57,7 +57,7 @@ def create(cfg):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(head_dim=64), -4), (dict(n_heads=3), -2), (dict(n_heads=16, n_kv_heads=2), -4),
-    (dict(mask_id=1024), -1), (dict(mask_id=-1), -1), (dict(vocab=1000), -4),
+    (dict(mask_id=1024), -1), (dict(mask_id=-1), -1), (dict(vocab=1000), -4), (dict(vocab=1152), -4),
     (dict(d_ffn=500), -4), (dict(rope_base=float("nan")), -1), (dict(rms_eps=0.0), -1),
     (dict(n_layers=0), -2),
 ])
@@ -156,6 +156,8 @@ def test_op_validation():
     assert lib.dlm_op_gemm(FAKE, FAKE, FAKE, 32, 128, 128, 64, 128, 0, FAKE, 1 << 30, None) == -2
     assert lib.dlm_op_lm_head(FAKE, 4, 128, FAKE, 1024, 1024, FAKE, FAKE, None, None, FAKE, 1 << 30,
                               None) == -1
+    # the head's vocabulary tiles are 256 wide
+    assert lib.dlm_op_lm_head(FAKE, 4, 128, FAKE, 1152, 0, FAKE, FAKE, None, None, FAKE, 1 << 30, None) == -2
     assert lib.dlm_op_attention(FAKE, 128, FAKE, FAKE, FAKE, None, 0, 1, 16, 4, 2, 64, 64, 0, 16, FAKE,
                                 1 << 30, None) == -4
     assert lib.dlm_op_attention(FAKE, 128, FAKE, FAKE, FAKE, None, 0, 1, 16, 4, 2, 32, 64, 0, 65, FAKE,
