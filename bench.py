@@ -83,10 +83,10 @@ def traffic_for(kernel: str, batch: int):
 
 TIMERS = {"lm_head": 0, "attention": 1, "gate_up": 2, "down": 3, "qkv": 4}
 
-# LM-head launches in a counter run: the tiled kernel (batch 32) and the skinny
-# one (batch 1), told apart from the other GEMMs by the head epilogue's template
-# argument (k_gemm_tiled<EPI, ...>, k_gemm_skinny<MT, EPI, ...>; EPI_HEAD = 3).
-HEAD_KERNELS = {"lm_head_b32": re.compile(r"k_gemm_tiled<3,"), "lm_head_b1": re.compile(r"k_gemm_skinny<\d+, 3,")}
+# LM-head launches in a counter run, told apart from the other GEMMs by the
+# head epilogue's template argument and the tile (k_gemm_tiled<EPI, BN, BM, ...>,
+# EPI_HEAD = 3): 256 x 256 tiles at batch 32, 256 x 64 tiles at batch 1.
+HEAD_KERNELS = {"lm_head_b32": re.compile(r"k_gemm_tiled<3, 256, 256,"), "lm_head_b1": re.compile(r"k_gemm_tiled<3, 256, 64,")}
 COPY_KERNEL = re.compile(r"copyBuffer")
 
 

@@ -27,8 +27,9 @@ enum { DLM_EPI_STORE_BF16 = 0, DLM_EPI_RESIDUAL_F32 = 1, DLM_EPI_SWIGLU = 2 };
  *                             rows interleaved by 16 (as dlm_weights.wgu);
  *                             out = silu(gate) * up, silu(z) = z / (1 + e^-z)
  * Requirements: N a multiple of 128; K a multiple of 256, or of 64 up to 256.
- * ws: dlm_op_gemm_workspace_bytes(M, N, K) bytes (zero with the current
- * kernels; ws may then be NULL). */
+ * ws: dlm_op_gemm_workspace_bytes(M, N, K) bytes, 256-byte aligned: fp32
+ * partial products when K is split over workgroups (short products, M <= 64);
+ * when that size is 0, ws may be NULL.  WORKSPACE if it is too small. */
 size_t dlm_op_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K);
 dlm_status dlm_op_gemm(const void* a, const void* w, void* out, int32_t M, int32_t N, int32_t K, int32_t lda,
                        int32_t ldc, int32_t epilogue, void* ws, size_t ws_bytes, void* stream);

@@ -95,6 +95,7 @@ struct PassBufs {
   int* rows;
   int* count;
   float4* head_part;
+  float* kpart;  // K-split partials of the layer projections (short passes only)
   size_t bytes;
 };
 
@@ -127,6 +128,20 @@ size_t head_part_records(const dlm_config& c, int R, bool bound) {
   return r;
 }
 
+// Workspace of the largest K-split layer projection over R rows (or, for a
+// bound, over any row count up to R).
+size_t layer_gemm_ws(const dlm_config& c, int R) {
+  const int d = c.d_model, qd = c.n_heads * c.head_dim;
+  size_t b = 0;
+  for (int r : {R, std::min(R, 64)}) {
+    b = std::max(b, gemm_workspace_bytes(r, qkv_dim(c), d));
+    b = std::max(b, gemm_workspace_bytes(r, d, qd));
+    b = std::max(b, gemm_workspace_bytes(r, 2 * c.d_ffn, d));
+    b = std::max(b, gemm_workspace_bytes(r, d, c.d_ffn));
+  }
+  return b;
+}
+
 PassBufs carve(const dlm_config& c, uintptr_t base, int R, int B, int Lq, int max_kv, bool bound) {
   Carver cv{base};
   PassBufs p{};
@@ -143,6 +158,7 @@ PassBufs carve(const dlm_config& c, uintptr_t base, int R, int B, int Lq, int ma
   p.rows = cv.take<int>(R);
   p.count = cv.take<int>(1);
   p.head_part = cv.take<float4>(head_part_records(c, R, bound));
+  p.kpart = cv.take<float>(layer_gemm_ws(c, R) / sizeof(float));
   p.bytes = align256(cv.off);
   return p;
 }
@@ -184,6 +200,7 @@ dlm_status run_layers(const dlm_model* m, const dlm_kv* kv, const int32_t* token
     bf16_t* vc = static_cast<bf16_t*>(kv->v) + l * lkv;
     if (l > 0) DLM_TRY(rmsnorm(p.x, R, d, m->attn_norm[l], c.rms_eps, p.xn, nullptr, nullptr, s), "rmsnorm");
     GemmArgs g{};
+    g.kpart = p.kpart;
     g.a = p.xn;
     g.w = m->wqkv[l];
     g.out = p.qkv;
@@ -498,10 +515,8 @@ dlm_status dlm_append_block(const dlm_model* m, const dlm_kv* kv, int32_t* prefi
 // ------------------------------------------------------------ ops ----
 
 size_t dlm_op_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K) {
-  (void)M;
-  (void)N;
-  (void)K;
-  return 0;
+  if (M < 1 || N < 1 || K < 1) return 0;
+  return align256(gemm_workspace_bytes(M, N, K));
 }
 
 dlm_status dlm_op_gemm(const void* a, const void* w, void* out, int32_t M, int32_t N, int32_t K, int32_t lda,
@@ -514,10 +529,12 @@ dlm_status dlm_op_gemm(const void* a, const void* w, void* out, int32_t M, int32
   if (epilogue < 0 || epilogue > 2) return fail(DLM_ERR_INVALID_ARG, "epilogue %d", epilogue);
   const int cols = epilogue == DLM_EPI_SWIGLU ? N / 2 : N;
   if (ldc < cols || ldc % 8) return fail(DLM_ERR_SHAPE, "ldc %d", ldc);
-  (void)ws;
-  (void)ws_bytes;
+  const size_t need = gemm_workspace_bytes(M, N, K);
+  if (need > 0 && (!ws || ws_bytes < need || reinterpret_cast<uintptr_t>(ws) % 256))
+    return fail(DLM_ERR_WORKSPACE, "gemm needs %zu bytes of 256-byte aligned workspace, got %zu", need, ws_bytes);
   hipStream_t s = static_cast<hipStream_t>(stream);
   GemmArgs g{};
+  g.kpart = static_cast<float*>(ws);
   g.a = a;
   g.w = w;
   g.out = out;

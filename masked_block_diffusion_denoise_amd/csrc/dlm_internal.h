@@ -17,6 +17,7 @@ enum GemmEpilogue : int {
   EPI_RESID_F32 = 1,   // out fp32 [M][ldc] += acc (residual stream)
   EPI_SWIGLU = 2,      // W rows gate/up interleaved in 16-row groups; out bf16 [M][N/2] = silu(g)*u
   EPI_HEAD = 3,        // per (row, vocab tile) partial max / sum exp / argmax; optional fp32 logits
+  EPI_SPLITK = 4,      // internal: fp32 partial products of one K range, reduced by a second kernel
 };
 
 struct GemmArgs {
@@ -32,9 +33,16 @@ struct GemmArgs {
   const int* logit_rows; // optional: logits of result row m go to row logit_rows[m]
   int mask_id;
   int* nonfinite;       // device counter, incremented on non-finite logits
+  // K-split (set by gemm() when gemm_ksplit() > 1): fp32 [ksplit][M][N] partials
+  float* kpart;         // workspace of gemm_workspace_bytes(M, N, K) bytes, from the caller
+  int ksplit;
 };
 
 int gemm_head_tile_n(int M);                       // vocab columns per EPI_HEAD partial
+// Number of K ranges gemm() splits an (M, N, K) product into (1: no split; the
+// LM head never splits), and the workspace (g.kpart) it then needs.
+int gemm_ksplit(int M, int N, int K);
+size_t gemm_workspace_bytes(int M, int N, int K);
 hipError_t gemm(const GemmArgs& g, GemmEpilogue epi, hipStream_t s);
 
 // --------------------------------------------------------- attention ----

@@ -6,16 +6,14 @@
 // an MFMA result holds consecutive output columns of one row and stores them as
 // one vector.
 //
-// Skinny tiling (M <= 64, one denoise canvas at batch 1-2, layer projections):
-// the weight matrix is read exactly once, streamed from HBM straight into MFMA
-// operand registers (v_mfma_f32_16x16x32_bf16), K split over the wavefronts of a
-// workgroup and summed through LDS -- no cross-workgroup reduction (whose
-// release fence would write back the L2 of an XCD).
-//
-// Tiled (M > 64, and the LM head at any M): 256 x 256, 256 x 128, 256 x 64 or
-// 128 x 128 output tiles, 32-deep K stages in a ring of LDS buffers filled by
+// One tiled kernel for every shape: 256 x 256, 256 x 128, 256 x 64, 128 x 128
+// or 128 x 64 output tiles, 32-deep K stages in a ring of LDS buffers filled by
 // direct global-to-LDS loads, each wavefront a block of
-// v_mfma_f32_32x32x16_bf16 tiles.
+// v_mfma_f32_32x32x16_bf16 tiles.  Short products (one canvas at batch 1-2)
+// are HBM-bound: their activation rows are loaded once per workgroup and shared
+// from LDS, and when there are too few weight tiles to fill the chip K is split
+// over workgroups, the fp32 partials summed in a fixed order by a second kernel
+// (no cross-workgroup atomics or fences).
 #include <algorithm>
 
 #include "dlm_device.h"
@@ -68,121 +66,6 @@ __device__ __forceinline__ void store_quad(const GemmArgs& g, int m, int n, cons
     x.z += v[2];
     x.w += v[3];
     *reinterpret_cast<float4*>(o) = x;
-  }
-}
-
-// ======================================================= skinny tiling ====
-// WAVES wavefronts per workgroup: NG groups of 16 weight rows times KP = WAVES/NG
-// parts of K.  Each wavefront streams its 16 weight rows over its K part from
-// HBM straight into MFMA operand registers (v_mfma_f32_16x16x32_bf16, weights as
-// the 16 x 32 A operand, activations as the B operand), two batches of four
-// 32-deep steps in flight; the K parts are summed through LDS in a fixed order.
-constexpr int SK_U = 4;  // 32-deep steps per load batch
-
-template <int MT, int EPI, int NG, int WAVES>
-__global__ void __launch_bounds__(WAVES * 64) k_gemm_skinny(GemmArgs g) {
-  constexpr int KP = WAVES / NG;
-  __shared__ float red[WAVES * MT * 4 * 64];
-
-  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int rg = w % NG, kp = w / NG;
-  const int tile = blockIdx.x;
-  const int n_w = (tile * NG + rg) * 16;
-  const int M = g.m_dev ? min(g.M, *g.m_dev) : g.M;
-  if (M <= 0) return;
-  const int nsteps = g.K / 32;
-  const int s_begin = kp * nsteps / KP, s_end = (kp + 1) * nsteps / KP;
-  const bf16_t* wp = static_cast<const bf16_t*>(g.w) + static_cast<size_t>(n_w + (lane & 15)) * g.K + 8 * (lane >> 4);
-  const bf16_t* ap[MT];
-#pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    const int r = min(t * 16 + (lane & 15), M - 1);  // rows past M repeat the last row; discarded
-    ap[t] = static_cast<const bf16_t*>(g.a) + static_cast<size_t>(r) * g.lda + 8 * (lane >> 4);
-  }
-
-  f32x4 acc[MT];
-#pragma unroll
-  for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // Operand registers of the two load batches.  They are zeroed up front: the
-  // loads and MFMAs below are guarded by the same step bound, but without
-  // explicit initial values the compiled pipeline was seen to consume
-  // registers left by earlier kernels (history-dependent garbage in the first
-  // 16-row tile) on wavefronts whose K part ends inside a batch.
-  u32x4 wa[SK_U], wb[SK_U], xa[SK_U][MT], xb[SK_U][MT];
-#pragma unroll
-  for (int u = 0; u < SK_U; ++u) {
-    wa[u] = wb[u] = u32x4{0, 0, 0, 0};
-#pragma unroll
-    for (int t = 0; t < MT; ++t) xa[u][t] = xb[u][t] = u32x4{0, 0, 0, 0};
-  }
-  // Loads are unconditional (steps past the end reload the last step, which is
-  // in bounds and never multiplied) so that the wait before each batch's MFMAs
-  // only covers that batch and the next batch stays in flight.
-#define SK_LOAD(WV, XV, S0)                                              \
-  _Pragma("unroll") for (int u = 0; u < SK_U; ++u) {                     \
-    const int st = min((S0) + u, s_last);                                \
-    WV[u] = ld16(wp + st * 32);                                          \
-    _Pragma("unroll") for (int t = 0; t < MT; ++t) XV[u][t] = ld16(ap[t] + st * 32); \
-  }
-#define SK_COMP(WV, XV, S0)                                              \
-  _Pragma("unroll") for (int u = 0; u < SK_U; ++u) {                     \
-    if ((S0) + u < s_end) {                                              \
-      _Pragma("unroll") for (int t = 0; t < MT; ++t)                     \
-        acc[t] = mfma16x16x32(as_bf16x8(WV[u]), as_bf16x8(XV[u][t]), acc[t]); \
-    }                                                                    \
-  }
-  const int s_last = max(s_end - 1, 0);
-  if (s_begin < s_end) SK_LOAD(wa, xa, s_begin);
-  for (int s = s_begin; s < s_end; s += 2 * SK_U) {
-    SK_LOAD(wb, xb, s + SK_U);
-    SK_COMP(wa, xa, s);
-    SK_LOAD(wa, xa, s + 2 * SK_U);
-    SK_COMP(wb, xb, s + SK_U);
-  }
-#undef SK_LOAD
-#undef SK_COMP
-
-  // lane holds D[n][m] for n = n_w + 4*(lane>>4) + r, m = t*16 + (lane & 15)
-  if (KP > 1 || EPI == EPI_SWIGLU) {
-#pragma unroll
-    for (int t = 0; t < MT; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) red[((w * MT + t) * 4 + r) * 64 + lane] = acc[t][r];
-    __syncthreads();
-  }
-  auto summed = [&](int group, int t, int r) {
-    float v = 0.f;
-    for (int k = 0; k < KP; ++k) v += red[(((k * NG + group) * MT + t) * 4 + r) * 64 + lane];
-    return v;
-  };
-
-  if (EPI == EPI_STORE_BF16 || EPI == EPI_RESID_F32) {
-    if (w >= NG) return;
-    const int nq = n_w + 4 * (lane >> 4);
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      const int m = t * 16 + (lane & 15);
-      float v[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = (KP > 1) ? summed(rg, t, r) : acc[t][r];
-      if (m < M) store_quad<EPI>(g, m, nq, v);
-    }
-  } else if (EPI == EPI_SWIGLU) {
-    // NG == 2: group 0 holds the 16 gate rows, group 1 the matching up rows
-    if (w != 0) return;
-    const int col = tile * 16 + 4 * (lane >> 4);
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      const int m = t * 16 + (lane & 15);
-      float v[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = silu_f(summed(0, t, r)) * summed(1, t, r);
-      if (m < M) {
-        bf16_t* o = static_cast<bf16_t*>(g.out) + static_cast<size_t>(m) * g.ldc + col;
-        *reinterpret_cast<u32x2*>(o) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-      }
-    }
   }
 }
 
@@ -262,6 +145,18 @@ __device__ __forceinline__ void lds_frags<2, 2>(uint32_t a, uint32_t b, u32x4 (&
       : "memory");
 }
 
+template <>
+__device__ __forceinline__ void lds_frags<1, 2>(uint32_t a, uint32_t b, u32x4 (&fa)[1], u32x4 (&fb)[2]) {
+  asm volatile(
+      "ds_read_b128 %0, %3\n\t"
+      "ds_read_b128 %1, %4\n\t"
+      "ds_read_b128 %2, %4 offset:2048\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(fa[0]), "=&v"(fb[0]), "=&v"(fb[1])
+      : "v"(a), "v"(b)
+      : "memory");
+}
+
 template <int EPI, int BN, int BM, int WN, int WM, int NBUF>
 __global__ void __launch_bounds__(WN * WM * 64) k_gemm_tiled(GemmArgs g) {
   constexpr int T = WN * WM * 64;
@@ -273,11 +168,13 @@ __global__ void __launch_bounds__(WN * WM * 64) k_gemm_tiled(GemmArgs g) {
   static_assert(NBUF >= 2 && NBUF <= 6, "wait ladder covers up to four later stages");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NBUF * STAGE];
 
+  // tile = (weight tile, K range, activation tile), activation tiles fastest
+  const int S = EPI == EPI_SPLITK ? g.ksplit : 1;
   const int nN = g.N / BN, nM = (g.M + BM - 1) / BM;
-  const int total = nN * nM, per = (total + 7) / 8;
+  const int total = nN * S * nM, per = (total + 7) / 8;
   const int tid_ = (blockIdx.x % 8) * per + blockIdx.x / 8;
   if (tid_ >= total) return;
-  const int n0 = (tid_ / nM) * BN, m0 = (tid_ % nM) * BM;
+  const int n0 = (tid_ / (nM * S)) * BN, split = (tid_ / nM) % S, m0 = (tid_ % nM) * BM;
   const int M = g.m_dev ? min(g.M, *g.m_dev) : g.M;
   if (m0 >= M) return;
 
@@ -302,11 +199,14 @@ __global__ void __launch_bounds__(WN * WM * 64) k_gemm_tiled(GemmArgs g) {
       src[b] = A + static_cast<size_t>(m) * g.lda + c * 8;
     }
   }
-  auto issue = [&](int kt) {
+  // this workgroup's stages: [k_lo, k_lo + nk) of the K / 32 stages
+  const int k_lo = split * (g.K / TL_BK) / S;
+  const int nk = (split + 1) * (g.K / TL_BK) / S - k_lo;
+  auto issue = [&](int kt) {  // kt counts this workgroup's stages from 0
     uint8_t* dst = lds + (kt % NBUF) * STAGE + w * BLK * 1024;
 #pragma unroll
     for (int b = 0; b < BLK; ++b)
-      load_lds16(src[b] + kt * TL_BK, dst + b * 1024);
+      load_lds16(src[b] + (k_lo + kt) * TL_BK, dst + b * 1024);
   };
 
   f32x16 acc[TN][TM];
@@ -317,7 +217,6 @@ __global__ void __launch_bounds__(WN * WM * 64) k_gemm_tiled(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int nk = g.K / TL_BK;
   const int arow = lane & 31, ahalf = lane >> 5;
   // fragment offsets within a stage for the two 16-deep steps (chunk 2s + ahalf)
   uint32_t fa_off[2], fb_off[2];
@@ -359,7 +258,22 @@ __global__ void __launch_bounds__(WN * WM * 64) k_gemm_tiled(GemmArgs g) {
 
   // lane holds D[n][m]: m = m0 + (wm*TM + j)*32 + (lane&31),
   // n = n0 + (wn*TN + i)*32 + 8*(r/4) + 4*(lane>>5) + r%4
-  if (EPI == EPI_STORE_BF16 || EPI == EPI_RESID_F32) {
+  if (EPI == EPI_SPLITK) {
+    float* part = g.kpart + static_cast<size_t>(split) * g.M * g.N;
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int j = 0; j < TM; ++j) {
+        const int m = m0 + (wm * TM + j) * 32 + arow;
+        if (m >= M) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + (wn * TN + i) * 32 + 8 * q + 4 * ahalf;
+          *reinterpret_cast<float4*>(part + static_cast<size_t>(m) * g.N + n) =
+              make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+        }
+      }
+  } else if (EPI == EPI_STORE_BF16 || EPI == EPI_RESID_F32) {
 #pragma unroll
     for (int i = 0; i < TN; ++i)
 #pragma unroll
@@ -434,26 +348,69 @@ __global__ void __launch_bounds__(WN * WM * 64) k_gemm_tiled(GemmArgs g) {
   }
 }
 
+// Sum of the K-split partials in split order (deterministic), then the
+// epilogue; one thread per 4 output columns of one row.
+template <int EPI>
+__global__ void __launch_bounds__(256) k_splitk_reduce(GemmArgs g) {
+  const int cols = EPI == EPI_SWIGLU ? g.N / 2 : g.N;
+  const int q4 = cols / 4;
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= g.M * q4) return;
+  const int m = t / q4, c = (t % q4) * 4;
+  const size_t plane = static_cast<size_t>(g.M) * g.N;
+  const float* row = g.kpart + static_cast<size_t>(m) * g.N;
+  if (EPI == EPI_SWIGLU) {
+    // output column c of a 16-column group reads gate row 32*(c/16) + c%16 and
+    // the up row 16 further (gate/up rows interleaved by 16)
+    const int n = 32 * (c / 16) + c % 16;
+    float4 gs = make_float4(0.f, 0.f, 0.f, 0.f), us = gs;
+    for (int k = 0; k < g.ksplit; ++k) {
+      const float4 a = *reinterpret_cast<const float4*>(row + k * plane + n);
+      const float4 b = *reinterpret_cast<const float4*>(row + k * plane + n + 16);
+      gs.x += a.x; gs.y += a.y; gs.z += a.z; gs.w += a.w;
+      us.x += b.x; us.y += b.y; us.z += b.z; us.w += b.w;
+    }
+    bf16_t* o = static_cast<bf16_t*>(g.out) + static_cast<size_t>(m) * g.ldc + c;
+    *reinterpret_cast<u32x2*>(o) = u32x2{pack_bf16x2(silu_f(gs.x) * us.x, silu_f(gs.y) * us.y),
+                                         pack_bf16x2(silu_f(gs.z) * us.z, silu_f(gs.w) * us.w)};
+  } else {
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < g.ksplit; ++k) {
+      const float4 a = *reinterpret_cast<const float4*>(row + k * plane + c);
+      v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
+    }
+    store_quad<EPI>(g, m, c, v);
+  }
+}
+
 // ============================================================== host ====
 // LM-head vocabulary columns per partial record (the tiled kernels' BN).
 int gemm_head_tile_n(int) { return 256; }
 
-template <int EPI, int BN, int BM, int WN, int WM, int NBUF>
-static void launch_tiled(const GemmArgs& g, hipStream_t s) {
-  const int total = (g.N / BN) * ((g.M + BM - 1) / BM);
-  const int per = (total + 7) / 8;
-  hipLaunchKernelGGL((k_gemm_tiled<EPI, BN, BM, WN, WM, NBUF>), dim3(8 * per), dim3(WN * WM * 64), 0, s, g);
+// Short products (M <= 64 rows: one canvas at batch 1-2) stream their weights
+// once through 128 x 64 tiles; with too few weight tiles to fill the chip, K is
+// split so that about 512 workgroups (two per CU) stream disjoint weight
+// slices, each K range at least 8 stages deep.
+constexpr int SK_BN = 128, SK_BM = 64;
+
+int gemm_ksplit(int M, int N, int K) {
+  if (M > SK_BM) return 1;
+  const int tiles = N / SK_BN;
+  const int want = (512 + tiles - 1) / tiles;
+  return std::max(1, std::min(want, K / (8 * TL_BK)));
 }
 
-template <int MT, int EPI>
-static void launch_skinny(const GemmArgs& g, hipStream_t s) {
-  if constexpr (EPI == EPI_SWIGLU) {
-    hipLaunchKernelGGL((k_gemm_skinny<MT, EPI, 2, 4>), dim3(g.N / 32), dim3(256), 0, s, g);
-  } else if (g.N / 16 < 512) {
-    hipLaunchKernelGGL((k_gemm_skinny<MT, EPI, 1, 8>), dim3(g.N / 16), dim3(512), 0, s, g);
-  } else {
-    hipLaunchKernelGGL((k_gemm_skinny<MT, EPI, 1, 4>), dim3(g.N / 16), dim3(256), 0, s, g);
-  }
+size_t gemm_workspace_bytes(int M, int N, int K) {
+  const int S = gemm_ksplit(M, N, K);
+  return S > 1 ? static_cast<size_t>(S) * M * N * sizeof(float) : 0;
+}
+
+template <int EPI, int BN, int BM, int WN, int WM, int NBUF>
+static void launch_tiled(const GemmArgs& g, hipStream_t s) {
+  const int S = EPI == EPI_SPLITK ? g.ksplit : 1;
+  const int total = (g.N / BN) * S * ((g.M + BM - 1) / BM);
+  const int per = (total + 7) / 8;
+  hipLaunchKernelGGL((k_gemm_tiled<EPI, BN, BM, WN, WM, NBUF>), dim3(8 * per), dim3(WN * WM * 64), 0, s, g);
 }
 
 template <int EPI>
@@ -468,13 +425,18 @@ static hipError_t launch_epi(const GemmArgs& g, hipStream_t s) {
       launch_tiled<EPI, 256, 128, 4, 2, 3>(g, s);
     else
       launch_tiled<EPI, 256, 256, 4, 2, 4>(g, s);
-  } else if (g.M <= 64) {
-    if (g.M <= 16)
-      launch_skinny<1, EPI>(g, s);
-    else if (g.M <= 32)
-      launch_skinny<2, EPI>(g, s);
-    else
-      launch_skinny<4, EPI>(g, s);
+  } else if (g.M <= SK_BM) {
+    const int S = gemm_ksplit(g.M, g.N, g.K);
+    if (S > 1) {
+      if (!g.kpart) return hipErrorInvalidValue;
+      GemmArgs h = g;
+      h.ksplit = S;
+      launch_tiled<EPI_SPLITK, SK_BN, SK_BM, 4, 1, 6>(h, s);
+      const int cols = EPI == EPI_SWIGLU ? g.N / 2 : g.N;
+      hipLaunchKernelGGL((k_splitk_reduce<EPI>), dim3((g.M * (cols / 4) + 255) / 256), dim3(256), 0, s, h);
+    } else {
+      launch_tiled<EPI, SK_BN, SK_BM, 4, 1, 6>(g, s);
+    }
   } else {
     // 256 x 256 tiles where they still give at least one wave of workgroups
     // (the SwiGLU gate/up projection); 128 x 128 otherwise
