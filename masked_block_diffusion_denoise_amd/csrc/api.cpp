@@ -115,11 +115,7 @@ size_t attn_floats(const dlm_config& c, int R, int B, int Lq, int max_kv) {
     const int splits = attn_splits(a, nullptr);
     return attn_partial_floats(splits, B * Lq, c.n_heads, c.head_dim);
   }
-  const long s1 = (max_kv + 127) / 128;
-  const long s2 = (16384L + static_cast<long>(R) * c.n_kv_heads - 1) / (static_cast<long>(R) * c.n_kv_heads) + 1;
-  const long splits = std::max(1L, std::min(s1, s2));
-  if (splits <= 1) return 0;
-  return static_cast<size_t>(splits) * R * c.n_heads * (c.head_dim + 2);
+  return attn_partial_floats_bound(R, c.n_heads, c.n_kv_heads, c.head_dim, max_kv);
 }
 
 size_t head_part_records(const dlm_config& c, int R, bool bound) {

@@ -33,9 +33,15 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libdlm)")
 
 
+# Per-source flags.  Attention keeps its output accumulators in VGPRs: its
+# online-softmax rescale touches them with vector ALU code, and in AGPRs every
+# tile would pay a copy of all of them (MFMA results default to AGPRs).
+SOURCE_FLAGS = {"k_attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", os.path.join(HERE, src), "-o", obj]
+    cmd = [hipcc(), *FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(HERE, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

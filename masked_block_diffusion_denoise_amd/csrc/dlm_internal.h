@@ -62,6 +62,8 @@ struct AttnArgs {
 };
 int attn_splits(const AttnArgs& a, int* chunk_out);
 size_t attn_partial_floats(int splits, int rows, int H, int hd);
+// bound of attn_partial_floats over every B, Lq with B*Lq <= R and max_kv keys
+size_t attn_partial_floats_bound(int R, int H, int G, int hd, int max_kv);
 hipError_t attention(const AttnArgs& a, hipStream_t s);
 
 // ------------------------------------------------------------ small ----

@@ -8,16 +8,23 @@
 // this kernel runs, the denoise pass is plain unmasked attention over keys
 // [0, P_b + L) and the causal pass masks keys after the query's position.
 //
-// One workgroup = one (row b, KV head g, block of 32 queries, key split); its
-// wavefronts are the query heads of the group.  Per 32-key tile:
+// One workgroup = one (row b, KV head g, block of 32 queries, key range); its
+// wavefronts are the query heads of the group, which share every K/V tile.
+// Per 32-key tile:
 //   S^T[key][query] = K_tile * Q^T      (v_mfma_f32_32x32x16_bf16, Q in registers)
 //   online softmax per query (each lane owns one query column)
 //   O^T[d][query] += V_tile^T * P^T     (P reused from the S registers as bf16)
-// K rows are staged in LDS in a permuted order (bits 2 and 3 of the key index
-// swapped) so that the S accumulator registers of a lane line up with eight
-// consecutive keys -- the layout of the V cache, which stores blocks of 16 keys
-// with the key index fastest ([cap/16][hd][16]).  So the V operand is one
-// 16-byte LDS read per MFMA and no transpose is needed anywhere.
+// K rows are read in a permuted order (bits 2 and 3 of the key index swapped)
+// so that the S accumulator registers of a lane line up with eight consecutive
+// keys -- the layout of the V cache, which stores blocks of 16 keys with the key
+// index fastest ([cap/16][hd][16]).  So the V operand is one 16-byte LDS read per
+// MFMA and no transpose is needed anywhere.
+//
+// K/V tiles stream through a ring of NBUF LDS stages filled by direct
+// global-to-LDS loads (global_load_lds_dwordx4), NBUF - 1 tiles in flight, one
+// wait + barrier per tile; fragments are read in inline asm that waits for its
+// own reads (the compiler cannot tell the ring stages apart and would otherwise
+// drain every load before each read).
 #include <algorithm>
 
 #include "dlm_device.h"
@@ -26,172 +33,287 @@
 namespace dlm {
 
 constexpr int KT = 32;          // keys per tile
-constexpr int MIN_CHUNK = 128;  // minimum keys per split
+constexpr int MIN_CHUNK = 256;  // minimum keys per split (8 tiles)
+// Launch shapes.  Wide batches (many (row, group) pairs): about 512 workgroups,
+// two per CU, each with a 3-stage ring -- the other workgroup on the CU hides
+// latency.  Narrow batches (batch 1-4): about 256 workgroups with a 6-stage ring,
+// each workgroup alone on its CU with five tiles in flight.
+constexpr int WIDE_BASE = 128;   // (row, group, query block) count from which a batch is wide
+constexpr int WIDE_TARGET = 512, WIDE_NBUF = 3;
+constexpr int NARROW_TARGET = 256, NARROW_NBUF = 6;
+constexpr float RESCALE = 8.f;  // lazy-rescale threshold (log2 units)
 
-// K rows in LDS: 16-byte chunks XOR-swizzled by the row so that the 32 rows read
-// by one MFMA operand load spread over the banks.
-__device__ __forceinline__ int kswz(int row, int chunk, int chunks) {
-  const int mask = chunks >= 8 ? 7 : chunks - 1;
-  return row * chunks * 8 + ((chunk ^ (row & mask)) << 3);
+__device__ __forceinline__ uint32_t att_lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p));
 }
 
-template <int HD, int GS>
-__global__ void __launch_bounds__(GS * 64) k_attn(AttnArgs a, int chunk_len) {
-  constexpr int KCH = HD / 8;  // 16-byte chunks per K row
-  __shared__ __attribute__((aligned(16))) bf16_t ks[KT * HD];
-  __shared__ __attribute__((aligned(16))) bf16_t vs[KT * HD];  // [2][HD][16]
+__device__ __forceinline__ void att_load_lds16(const void* src, void* lds_dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
+}
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+template <int N>
+__device__ __forceinline__ void att_wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"i"(N) : "memory");
+}
+
+// K rows in LDS: row r (key k0 + r) holds its 16-byte chunks XOR-swizzled.  The
+// LDS serves 16 lanes x 16 bytes per cycle; the 16 rows one quarter of an
+// operand read touches must land in 16 distinct 16-byte bank groups: with
+// 256-byte rows (hd 128) the chunk is XOR-ed with the row's low 4 bits, with
+// 64-byte rows (hd 32, four rows per 256 bytes) with row bits 2-3.
+template <int HD>
+__device__ __forceinline__ int kxor(int row) {
+  return HD >= 128 ? (row & 15) : ((row >> 2) & 3);
+}
+
+// V rows ([blk][d] of 2 x 16 bytes): the two halves of row d are swapped when
+// bit 3 of d is set, so the 16 consecutive d one read quarter touches cover all
+// 16 bank groups.
+__device__ __forceinline__ int vxor(int vrow) { return (vrow >> 3) & 1; }
+
+// Fragment reads (each waits for its own reads before returning).
+template <int N>
+__device__ __forceinline__ void lds_read_n(const uint32_t (&addr)[N], u32x4 (&f)[N]);
+
+template <>
+__device__ __forceinline__ void lds_read_n<8>(const uint32_t (&a)[8], u32x4 (&f)[8]) {
+  asm volatile(
+      "ds_read_b128 %0, %8\n\tds_read_b128 %1, %9\n\tds_read_b128 %2, %10\n\tds_read_b128 %3, %11\n\t"
+      "ds_read_b128 %4, %12\n\tds_read_b128 %5, %13\n\tds_read_b128 %6, %14\n\tds_read_b128 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2]), "=&v"(f[3]), "=&v"(f[4]), "=&v"(f[5]), "=&v"(f[6]), "=&v"(f[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+      : "memory");
+}
+
+template <>
+__device__ __forceinline__ void lds_read_n<4>(const uint32_t (&a)[4], u32x4 (&f)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2]), "=&v"(f[3])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+      : "memory");
+}
+
+template <>
+__device__ __forceinline__ void lds_read_n<1>(const uint32_t (&a)[1], u32x4 (&f)[1]) {
+  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(f[0]) : "v"(a[0]) : "memory");
+}
+
+template <>
+__device__ __forceinline__ void lds_read_n<2>(const uint32_t (&a)[2], u32x4 (&f)[2]) {
+  asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+               : "=&v"(f[0]), "=&v"(f[1])
+               : "v"(a[0]), "v"(a[1])
+               : "memory");
+}
+
+template <int HD, int GS, int ATT_NBUF>
+__global__ void __launch_bounds__(GS * 64) k_attn(AttnArgs a, int chunk_len) {
+  constexpr int KCH = HD / 8;              // 16-byte chunks per key row
+  constexpr int TILE_K = KT * HD * 2;      // bytes of a K tile (= bytes of a V tile)
+  constexpr int STAGE = 2 * TILE_K;
+  constexpr int NBLK = STAGE / 1024;       // 1 KB load blocks per stage
+  constexpr int BLK = NBLK / GS;           // ... per wavefront
+  static_assert(NBLK % GS == 0 && BLK >= 1, "stage must split evenly over the wavefronts");
+  constexpr int NS = HD / 16;              // 16-deep steps of the S product
+  constexpr int ND = HD / 32;              // 32-row blocks of the output
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[ATT_NBUF * STAGE];
+
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int split = blockIdx.x, qb = blockIdx.y;
   const int b = blockIdx.z / a.G, g = blockIdx.z % a.G;
   const int h = g * GS + w;
   const int p0 = (a.prefix ? a.prefix[b] : 0) + a.pos_offset;
   const int kv_len = min(p0 + a.Lq, a.cap);  // never read past the cache
-  const int jq = qb * 32 + (lane & 31);  // this lane's query (block-relative)
+  const int jq = qb * 32 + (lane & 31);      // this lane's query (block-relative)
   const int half = lane >> 5;
 
-  int kbeg = split * chunk_len;
+  const int kbeg = split * chunk_len;
   int kend = min(kv_len, kbeg + chunk_len);
   if (a.causal) kend = min(kend, p0 + min(qb * 32 + 32, a.Lq));
+  const int ntiles = kend > kbeg ? (kend - kbeg + KT - 1) / KT : 0;
 
   const int splits = gridDim.x;
   const size_t mrow = static_cast<size_t>(b) * a.Lq + jq;  // output row
 
   // queries, this lane's column: d = s*16 + 8*half .. +8
-  bf16x8 qf[HD / 16];
+  bf16x8 qf[NS];
   {
     const bf16_t* qp = static_cast<const bf16_t*>(a.q) + mrow * a.ldq + h * HD + 8 * half;
 #pragma unroll
-    for (int s = 0; s < HD / 16; ++s)
-      qf[s] = as_bf16x8(jq < a.Lq ? ld16(qp + s * 16) : u32x4{0, 0, 0, 0});
+    for (int s = 0; s < NS; ++s) qf[s] = as_bf16x8(jq < a.Lq ? ld16(qp + s * 16) : u32x4{0, 0, 0, 0});
   }
 
-  f32x16 o[HD / 32];
+  f32x16 o[ND];
 #pragma unroll
-  for (int c = 0; c < HD / 32; ++c)
+  for (int c = 0; c < ND; ++c)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[c][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
   const float scale = 1.4426950408889634f / sqrtf(static_cast<float>(HD));  // log2(e)/sqrt(hd)
   const int qpos = p0 + jq;
 
-  const bf16_t* kc = static_cast<const bf16_t*>(a.kc) + (static_cast<size_t>(b) * a.G + g) * a.cap * HD;
-  const bf16_t* vc = static_cast<const bf16_t*>(a.vc) + (static_cast<size_t>(b) * a.G + g) * a.cap * HD;
+  const size_t head_off = (static_cast<size_t>(b) * a.G + g) * a.cap * HD;
+  const bf16_t* kc = static_cast<const bf16_t*>(a.kc) + head_off;
+  const bf16_t* vc = static_cast<const bf16_t*>(a.vc) + head_off;
 
-  // staging: K tile = KT*KCH chunks, V tile = 2*HD*2 chunks (16 B each)
-  constexpr int NKC = KT * KCH, NVC = 2 * HD * 2;
-  constexpr int PER = (NKC + NVC + GS * 64 - 1) / (GS * 64);
-  u32x4 st[PER];
-  auto gload = [&](int k0) {
+  // Load block q of a stage, lane l -> 16-byte slot 64q + l of the stage.  K
+  // blocks (q < NBLK/2): slot -> (row, physical chunk) -> logical chunk of key
+  // k0 + row.  V blocks: the V tile is contiguous in the blocked cache layout
+  // ([2][HD][16] keys from k0), slot -> (vrow, physical half) -> logical half.
+  // Both tile bases sit at element k0*HD of their cache.
+  const bf16_t* src[BLK];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int e = threadIdx.x + i * GS * 64;
-      u32x4 v = u32x4{0, 0, 0, 0};
-      if (e < NKC) {
-        const int row = e / KCH, ch = e % KCH;
-        const int key = k0 + row;
-        if (key < kend) v = ld16(kc + static_cast<size_t>(key) * HD + ch * 8);
-      } else if (e < NKC + NVC) {
-        const int f = e - NKC;  // [blk][d][half]
-        const int blk = f / (HD * 2), d = (f / 2) % HD, hh = f & 1;
-        const int key0 = k0 + blk * 16 + hh * 8;
-        if (key0 < kend) {
-          v = ld16(vc + (static_cast<size_t>(k0 / 16 + blk) * HD + d) * 16 + hh * 8);
-          const int valid = kend - key0;  // zero keys past the end (stale slots)
-          if (valid < 8) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              uint32_t x = v[u];
-              if (2 * u >= valid) x &= 0xffff0000u;
-              if (2 * u + 1 >= valid) x &= 0x0000ffffu;
-              v[u] = x;
-            }
-          }
-        }
-      }
-      st[i] = v;
+  for (int i = 0; i < BLK; ++i) {
+    const int q = w * BLK + i;
+    if (q < NBLK / 2) {
+      const int slot = q * 64 + lane;
+      const int row = slot / KCH, pc = slot % KCH;
+      src[i] = kc + row * HD + (pc ^ kxor<HD>(row)) * 8;
+    } else {
+      const int slot = (q - NBLK / 2) * 64 + lane;
+      const int vrow = slot >> 1, ph = slot & 1;
+      src[i] = vc + vrow * 16 + (ph ^ vxor(vrow)) * 8;
     }
-  };
-  auto lstore = [&]() {
+  }
+  auto issue = [&](int t) {  // tile t of this workgroup's key range
+    uint8_t* dst = lds + (t % ATT_NBUF) * STAGE + w * BLK * 1024;
+    const size_t off = static_cast<size_t>(kbeg + t * KT) * HD;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int e = threadIdx.x + i * GS * 64;
-      if (e < NKC) {
-        const int row = e / KCH, ch = e % KCH;
-        st16(&ks[kswz(row, ch, KCH)], st[i]);
-      } else if (e < NKC + NVC) {
-        st16(&vs[(e - NKC) * 8], st[i]);
-      }
-    }
+    for (int i = 0; i < BLK; ++i) att_load_lds16(src[i] + off, dst + i * 1024);
   };
 
-  // physical key row read by this lane in the S product (bits 2 and 3 swapped)
+  // fragment offsets within a stage
   const int ar = lane & 31;
-  const int krow = (ar & ~12) | ((ar & 4) << 1) | ((ar & 8) >> 1);
-
-  if (kbeg < kend) {
-    gload(kbeg);
-    lstore();
-    __syncthreads();
-    for (int k0 = kbeg; k0 < kend; k0 += KT) {
-      const bool more = k0 + KT < kend;
-      if (more) gload(k0 + KT);
-
-      f32x16 sacc;
+  const int krow = (ar & ~12) | ((ar & 4) << 1) | ((ar & 8) >> 1);  // bits 2 and 3 swapped
+  uint32_t koff[NS];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+  for (int s = 0; s < NS; ++s) koff[s] = krow * HD * 2 + (((2 * s + half) ^ kxor<HD>(krow)) << 4);
+  // V row d = dc*32 + ar of block c; the bank swizzle only depends on ar
+  const uint32_t voff = TILE_K + ar * 32 + ((half ^ vxor(ar)) << 4);
+  const uint32_t lbase = att_lds_addr(lds);
+
 #pragma unroll
-      for (int s = 0; s < HD / 16; ++s) {
-        const bf16x8 kf = as_bf16x8(ld16(&ks[kswz(krow, 2 * s + half, KCH)]));
-        sacc = mfma32x32x16(kf, qf[s], sacc);
+  for (int p = 0; p < ATT_NBUF - 1; ++p)
+    if (p < ntiles) issue(p);
+  for (int t = 0; t < ntiles; ++t) {
+    // vmcnt counts at most 63: waiting for fewer outstanding loads is only stricter
+    const int later = min(ntiles - 1 - t, ATT_NBUF - 2);
+    if (later >= 4)
+      att_wait_barrier<std::min(4 * BLK, 63)>();
+    else if (later == 3)
+      att_wait_barrier<std::min(3 * BLK, 63)>();
+    else if (later == 2)
+      att_wait_barrier<2 * BLK>();
+    else if (later == 1)
+      att_wait_barrier<BLK>();
+    else
+      att_wait_barrier<0>();
+    if (t + ATT_NBUF - 1 < ntiles) issue(t + ATT_NBUF - 1);
+    const int k0 = kbeg + t * KT;
+    const uint32_t sb = lbase + (t % ATT_NBUF) * STAGE;
+
+    // two independent accumulation chains (even / odd steps) halve the MFMA
+    // dependency chain of the S product
+    f32x16 sacc, sodd;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sacc[r] = sodd[r] = 0.f;
+    // fragment reads in batches of KB (two batches at hd 128: register pressure);
+    // KB is even so that each batch feeds both chains
+    constexpr int KB = NS >= 8 ? NS / 2 : NS;
+    static_assert(KB % 2 == 0 && NS % KB == 0, "batches of an even number of K fragments");
+#pragma unroll
+    for (int hs = 0; hs < NS; hs += KB) {
+      uint32_t ka[KB];
+      u32x4 kf[KB];
+#pragma unroll
+      for (int s = 0; s < KB; ++s) ka[s] = sb + koff[hs + s];
+      lds_read_n<KB>(ka, kf);
+#pragma unroll
+      for (int s = 0; s < KB; s += 2) {
+        sacc = mfma32x32x16(as_bf16x8(kf[s]), qf[hs + s], sacc);
+        sodd = mfma32x32x16(as_bf16x8(kf[s + 1]), qf[hs + s + 1], sodd);
       }
-      // register r holds key k0 + 16*(r/8) + 8*half + (r%8)
-      float mloc = -INFINITY;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sacc[r] += sodd[r];
+    // register r holds key k0 + 16*(r/8) + 8*half + (r%8).  Only the last tile
+    // of the range and causal passes need a mask.
+    const bool tail = k0 + KT > kend;
+    if (tail || a.causal) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = k0 + 16 * (r >> 3) + 8 * half + (r & 7);
-        float sv = sacc[r] * scale;
-        if (key >= kend || (a.causal && key > qpos)) sv = -INFINITY;
-        sacc[r] = sv;
-        mloc = fmaxf(mloc, sv);
+        if (key >= kend || (a.causal && key > qpos)) sacc[r] = -INFINITY;
       }
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, WAVE));
+    }
+    float mloc = sacc[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mloc = fmaxf(mloc, sacc[r]);
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, WAVE)) * scale;
+    // Lazy rescaling: the exponent reference m_run only moves when some query of
+    // the wavefront sees a score more than 2^RESCALE above it (then all lanes
+    // rescale together); otherwise p <= 2^RESCALE and the output accumulators,
+    // which live in AGPRs, are not touched.  o / l is unchanged by the choice.
+    if (__any(mloc > m_run + RESCALE)) {
       const float m_new = fmaxf(m_run, mloc);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = exp2f(m_run - m_use);
-      float lsum = 0.f;
+      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = exp2f(sacc[r] - m_use);
-        sacc[r] = p;
-        lsum += p;
-      }
-      lsum += __shfl_xor(lsum, 32, WAVE);
-      l_run = l_run * alpha + lsum;
-      m_run = m_new;
-#pragma unroll
-      for (int c = 0; c < HD / 32; ++c)
+      for (int c = 0; c < ND; ++c)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[c][r] *= alpha;
-      bf16x8 pb[2];
+      m_run = m_new;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    float lsum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(sacc[r], scale, -m_use));
+      sacc[r] = p;
+      lsum += p;
+    }
+    lsum += __shfl_xor(lsum, 32, WAVE);
+    l_run += lsum;
+    bf16x8 pb[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      u32x4 u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) u[e] = pack_bf16x2(sacc[8 * c + 2 * e], sacc[8 * c + 2 * e + 1]);
+      pb[c] = as_bf16x8(u);
+    }
+    // cache slots past the row's end may hold anything (also NaN): their values
+    // are zeroed in the fragments, not only their probabilities
+    constexpr int DH = ND > 1 ? ND / 2 : 1;  // output blocks per batch of V reads
+#pragma unroll
+    for (int d0 = 0; d0 < ND; d0 += DH) {
+      uint32_t va[2 * DH];
+      u32x4 vf[2 * DH];
+#pragma unroll
+      for (int dd = 0; dd < DH; ++dd)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) va[2 * dd + c] = sb + voff + c * (HD * 32) + (d0 + dd) * 1024;
+      lds_read_n<2 * DH>(va, vf);
+#pragma unroll
+      for (int dd = 0; dd < DH; ++dd)
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        u32x4 u;
+        const int dc = d0 + dd;
+        u32x4 x4 = vf[2 * dd + c];
+        if (tail) {
+          const int valid = kend - (k0 + 16 * c + 8 * half);  // keys of this fragment still in range
 #pragma unroll
-        for (int e = 0; e < 4; ++e) u[e] = pack_bf16x2(sacc[8 * c + 2 * e], sacc[8 * c + 2 * e + 1]);
-        pb[c] = as_bf16x8(u);
-      }
-#pragma unroll
-      for (int dc = 0; dc < HD / 32; ++dc)
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const bf16x8 vf = as_bf16x8(ld16(&vs[((c * HD) + dc * 32 + ar) * 16 + 8 * half]));
-          o[dc] = mfma32x32x16(vf, pb[c], o[dc]);
+          for (int u = 0; u < 4; ++u) {
+            uint32_t x = x4[u];
+            if (2 * u >= valid) x &= 0xffff0000u;
+            if (2 * u + 1 >= valid) x &= 0x0000ffffu;
+            x4[u] = x;
+          }
         }
-      __syncthreads();
-      if (more) {
-        lstore();
-        __syncthreads();
+        o[dc] = mfma32x32x16(as_bf16x8(x4), pb[c], o[dc]);
       }
     }
   }
@@ -202,7 +324,7 @@ __global__ void __launch_bounds__(GS * 64) k_attn(AttnArgs a, int chunk_len) {
     const float inv = (l_run > 0.f) ? 1.0f / l_run : 0.f;
     bf16_t* op = static_cast<bf16_t*>(a.o) + mrow * (a.H * HD) + h * HD + 4 * half;
 #pragma unroll
-    for (int dc = 0; dc < HD / 32; ++dc)
+    for (int dc = 0; dc < ND; ++dc)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         *reinterpret_cast<u32x2*>(op + dc * 32 + 8 * q) =
@@ -213,7 +335,7 @@ __global__ void __launch_bounds__(GS * 64) k_attn(AttnArgs a, int chunk_len) {
     const size_t base = (static_cast<size_t>(split) * rows + mrow) * a.H + h;
     float* po = a.part_o + base * HD + 4 * half;
 #pragma unroll
-    for (int dc = 0; dc < HD / 32; ++dc)
+    for (int dc = 0; dc < ND; ++dc)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         *reinterpret_cast<float4*>(po + dc * 32 + 8 * q) =
@@ -223,36 +345,55 @@ __global__ void __launch_bounds__(GS * 64) k_attn(AttnArgs a, int chunk_len) {
 }
 
 // Merge split partials: o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
+// One wavefront per (row, head): lane s holds split s's (m, l); each lane sums
+// HD/64 (or one) output dims over the splits in split order.
 template <int HD>
 __global__ void __launch_bounds__(256) k_attn_merge(AttnArgs a, int splits) {
-  constexpr int PER_BLK = 256 / HD;
   const int rows = a.B * a.Lq;
-  const int pair = blockIdx.x * PER_BLK + threadIdx.x / HD;  // (row, head)
-  const int d = threadIdx.x % HD;
+  const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);  // (row, head)
+  const int lane = threadIdx.x & 63;
   if (pair >= rows * a.H) return;
   const int mrow = pair / a.H, h = pair % a.H;
-  float mx = -INFINITY;
-  for (int s = 0; s < splits; ++s)
-    mx = fmaxf(mx, a.part_ml[((static_cast<size_t>(s) * rows + mrow) * a.H + h) * 2]);
+  auto at = [&](int s) { return (static_cast<size_t>(s) * rows + mrow) * a.H + h; };
+  float2 ml = make_float2(-INFINITY, 0.f);
+  if (lane < splits) ml = *reinterpret_cast<const float2*>(a.part_ml + at(lane) * 2);
+  float mx = ml.y > 0.f ? ml.x : -INFINITY;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, WAVE));
   const float mu = (mx == -INFINITY) ? 0.f : mx;
-  float l = 0.f, acc = 0.f;
+  const float wgt = (ml.y > 0.f) ? __builtin_amdgcn_exp2f(ml.x - mu) : 0.f;
+  const float l = wave_sum(wgt * ml.y);
+  constexpr int PER = HD >= 64 ? HD / 64 : 1;
+  float acc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+  const int d0 = lane * PER;
   for (int s = 0; s < splits; ++s) {
-    const size_t base = (static_cast<size_t>(s) * rows + mrow) * a.H + h;
-    const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + base * 2);
-    const float wgt = (ml.y > 0.f) ? exp2f(ml.x - mu) : 0.f;
-    l += wgt * ml.y;
-    if (wgt != 0.f) acc += wgt * a.part_o[base * HD + d];
+    const float ws = __shfl(wgt, s, WAVE);
+    if (ws != 0.f && d0 < HD) {
+      const float* po = a.part_o + at(s) * HD + d0;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) acc[e] += ws * po[e];
+    }
   }
-  static_cast<bf16_t*>(a.o)[static_cast<size_t>(mrow) * a.H * HD + h * HD + d] =
-      f32_to_bf16(l > 0.f ? acc / l : 0.f);
+  if (d0 < HD) {
+    bf16_t* op = static_cast<bf16_t*>(a.o) + static_cast<size_t>(mrow) * a.H * HD + h * HD + d0;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) op[e] = f32_to_bf16(l > 0.f ? acc[e] / l : 0.f);
+  }
 }
 
+// Key splits: enough (row, group, query block, split) workgroups for about one
+// per CU, each split at least MIN_CHUNK keys; no split when the batch already
+// fills the chip (the merge costs a pass over fp32 partials).  At most 64 splits
+// (one merge lane each).
 int attn_splits(const AttnArgs& a, int* chunk_out) {
   const int qblocks = (a.Lq + 31) / 32;
   const long base = static_cast<long>(qblocks) * a.B * a.G;
-  int splits = static_cast<int>((512 + base - 1) / base);
-  const int max_splits = (a.max_kv + MIN_CHUNK - 1) / MIN_CHUNK;
-  splits = std::max(1, std::min(splits, max_splits));
+  const long target = base >= WIDE_BASE ? WIDE_TARGET : NARROW_TARGET;
+  int splits = static_cast<int>((target + base - 1) / base);
+  const int max_splits = std::max(1, a.max_kv / MIN_CHUNK);
+  splits = std::max(1, std::min({splits, max_splits, 64}));
   int chunk = (a.max_kv + splits - 1) / splits;
   chunk = (chunk + KT - 1) / KT * KT;
   splits = (a.max_kv + chunk - 1) / chunk;
@@ -265,16 +406,26 @@ size_t attn_partial_floats(int splits, int rows, int H, int hd) {
   return static_cast<size_t>(splits) * rows * H * (hd + 2);
 }
 
+size_t attn_partial_floats_bound(int R, int H, int G, int hd, int max_kv) {
+  // splits <= min(ceil(max target / G), max_kv / MIN_CHUNK, 64) for any B, Lq with B*Lq <= R
+  const int target = std::max(WIDE_TARGET, NARROW_TARGET);
+  const int s = std::max(1, std::min({(target + G - 1) / G, max_kv / MIN_CHUNK, 64}));
+  return attn_partial_floats(s, R, H, hd);
+}
+
 template <int HD, int GS>
 static hipError_t launch(const AttnArgs& a, hipStream_t s) {
   int chunk = 0;
   const int splits = attn_splits(a, &chunk);
-  dim3 grid(splits, (a.Lq + 31) / 32, a.B * a.G);
-  hipLaunchKernelGGL((k_attn<HD, GS>), grid, dim3(GS * 64), 0, s, a, chunk);
+  const int qblocks = (a.Lq + 31) / 32;
+  dim3 grid(splits, qblocks, a.B * a.G);
+  if (static_cast<long>(qblocks) * a.B * a.G >= WIDE_BASE)
+    hipLaunchKernelGGL((k_attn<HD, GS, WIDE_NBUF>), grid, dim3(GS * 64), 0, s, a, chunk);
+  else
+    hipLaunchKernelGGL((k_attn<HD, GS, NARROW_NBUF>), grid, dim3(GS * 64), 0, s, a, chunk);
   if (splits > 1) {
     const int pairs = a.B * a.Lq * a.H;
-    const int per = 256 / HD;
-    hipLaunchKernelGGL((k_attn_merge<HD>), dim3((pairs + per - 1) / per), dim3(256), 0, s, a, splits);
+    hipLaunchKernelGGL((k_attn_merge<HD>), dim3((pairs + 3) / 4), dim3(256), 0, s, a, splits);
   }
   return hipGetLastError();
 }

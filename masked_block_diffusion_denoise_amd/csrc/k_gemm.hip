@@ -388,16 +388,18 @@ __global__ void __launch_bounds__(256) k_splitk_reduce(GemmArgs g) {
 int gemm_head_tile_n(int) { return 256; }
 
 // Short products (M <= 64 rows: one canvas at batch 1-2) stream their weights
-// once through 128 x 64 tiles; with too few weight tiles to fill the chip, K is
-// split so that about 512 workgroups (two per CU) stream disjoint weight
-// slices, each K range at least 8 stages deep.
+// once through 128 x 64 tiles.  With too few weight tiles to fill the chip, K is
+// split so that several hundred workgroups stream disjoint weight slices; each
+// K range stays at least 16 stages deep and at most 8 splits are made, since
+// every split adds an fp32 partial plane to write and reduce (measured best:
+// 3 splits for 224 tiles, 8 for 32-48 tiles).
 constexpr int SK_BN = 128, SK_BM = 64;
 
 int gemm_ksplit(int M, int N, int K) {
   if (M > SK_BM) return 1;
   const int tiles = N / SK_BN;
-  const int want = (512 + tiles - 1) / tiles;
-  return std::max(1, std::min(want, K / (8 * TL_BK)));
+  const int want = (640 + tiles - 1) / tiles;
+  return std::max(1, std::min({want, K / (16 * TL_BK), 8}));
 }
 
 size_t gemm_workspace_bytes(int M, int N, int K) {

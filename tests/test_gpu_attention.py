@@ -12,7 +12,7 @@ from masked_block_diffusion_denoise_amd import _lib as L
 pytestmark = pytest.mark.gpu
 
 
-def run_case(B, Lq, H, G, hd, prefix, pos_offset, causal, seed, check_rows=None):
+def run_case(B, Lq, H, G, hd, prefix, pos_offset, causal, seed, check_rows=None, poison=False):
     p0 = (np.zeros(B, np.int64) if prefix is None else np.asarray(prefix)) + pos_offset
     kv_len = p0 + Lq
     max_kv = int(kv_len.max())
@@ -20,6 +20,10 @@ def run_case(B, Lq, H, G, hd, prefix, pos_offset, causal, seed, check_rows=None)
     q = synth.normal(seed, 70, (B * Lq, H * hd), 1.0)
     k = synth.normal(seed, 71, (B, G, cap, hd), 1.0)
     v = synth.normal(seed, 72, (B, G, cap, hd), 1.0)
+    if poison:  # cache slots past a row's end may hold anything, NaN and Inf included
+        for b in range(B):
+            k[b, :, kv_len[b]:] = np.nan
+            v[b, :, kv_len[b]:] = np.inf
     vb = v.reshape(B, G, cap // 16, 16, hd).transpose(0, 1, 2, 4, 3)  # blocked layout
     tq, tk, tv = bf16(q), bf16(k), bf16(np.ascontiguousarray(vb))
     to = torch.zeros(B * Lq, H * hd, dtype=torch.bfloat16, device="cuda")
@@ -68,3 +72,12 @@ def test_attention_single_key_is_the_value():
 def test_attention_batch32_prefix4096():
     announce("attention b32 p4096")
     run_case(32, 32, 32, 8, 128, [4096] * 32, 0, 0, seed=7, check_rows=[0, 17, 31])
+
+
+@pytest.mark.parametrize("hd,H,G", [(32, 4, 2), (128, 32, 8)])
+@pytest.mark.parametrize("causal", [0, 1])
+def test_attention_ignores_slots_past_the_end(hd, H, G, causal):
+    announce(f"attention poisoned tail hd={hd} causal={causal}")
+    # ragged ends inside a 32-key tile, a split case (one row, long prefix) and a batch case
+    run_case(3, 16, H, G, hd, [5, 37, 301], 0, causal, seed=8, poison=True)
+    run_case(1, 32, H, G, hd, [2077], 0, causal, seed=9, poison=True)
