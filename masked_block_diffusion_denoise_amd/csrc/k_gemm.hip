@@ -226,6 +226,10 @@ __global__ void __launch_bounds__(WN * WM * 64) k_gemm_tiled(GemmArgs g) {
     fb_off[s] = BN * TL_ROW + swz(wm * TM * 32 + arow, 2 * s + ahalf);
   }
   const uint32_t lbase = lds_addr(lds);
+  // A wavefront whose activation rows all lie past the live rows (the ragged
+  // last row tile, e.g. the masked rows of the LM head) still loads its share of
+  // every stage and joins every barrier, but skips its reads and MFMAs.
+  const bool live = m0 + wm * TM * 32 < M;
 
 #pragma unroll
   for (int p = 0; p < NBUF - 1; ++p)
@@ -244,6 +248,7 @@ __global__ void __launch_bounds__(WN * WM * 64) k_gemm_tiled(GemmArgs g) {
     else
       wait_vm_barrier<0>();
     if (kt + NBUF - 1 < nk) issue(kt + NBUF - 1);
+    if (!live) continue;
     const uint32_t sb = lbase + (kt % NBUF) * STAGE;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
