@@ -33,10 +33,12 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libdlm)")
 
 
-# Per-source flags.  Attention keeps its output accumulators in VGPRs: its
-# online-softmax rescale touches them with vector ALU code, and in AGPRs every
-# tile would pay a copy of all of them (MFMA results default to AGPRs).
-SOURCE_FLAGS = {"k_attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# Per-source flags.  The MFMA kernels keep their accumulators in VGPRs: where a
+# loop-carried accumulator also meets vector ALU code (attention's online
+# softmax rescale, a GEMM wavefront that skips its MFMAs) the compiler otherwise
+# copies every accumulator between AGPRs and VGPRs on every iteration.
+VGPR_MFMA = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+SOURCE_FLAGS = {"k_attention.hip": VGPR_MFMA, "k_gemm.hip": VGPR_MFMA}
 
 
 def _compile(src: str) -> str:

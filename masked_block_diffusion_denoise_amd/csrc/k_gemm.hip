@@ -7,8 +7,8 @@
 // one vector.
 //
 // One tiled kernel for every shape: 256 x 256, 256 x 128, 256 x 64, 128 x 128
-// or 128 x 64 output tiles, 32-deep K stages in a ring of LDS buffers filled by
-// direct global-to-LDS loads, each wavefront a block of
+// or 128 x 64 output tiles, 32- or 64-deep K stages in a ring of LDS buffers
+// filled by direct global-to-LDS loads, each wavefront a block of
 // v_mfma_f32_32x32x16_bf16 tiles.  Short products (one canvas at batch 1-2)
 // are HBM-bound: their activation rows are loaded once per workgroup and shared
 // from LDS, and when there are too few weight tiles to fill the chip K is split
@@ -73,7 +73,7 @@ __device__ __forceinline__ void store_quad(const GemmArgs& g, int m, int n, cons
 // BN x BM output tile (weights x activations) per workgroup of WN x WM
 // wavefronts, each a (BN/WN) x (BM/WM) block of 32 x 32 MFMA tiles.
 //
-// K runs in 32-deep stages through a ring of NBUF LDS buffers filled by direct
+// K runs in BK-deep stages through a ring of NBUF LDS buffers filled by direct
 // global-to-LDS loads (global_load_lds_dwordx4: each lane's 16 bytes land at
 // the instruction's LDS base + 16 * lane), so NBUF - 1 stages are in flight
 // while one is multiplied, without staging registers.  One wait + barrier per
@@ -85,14 +85,18 @@ __device__ __forceinline__ void store_quad(const GemmArgs& g, int m, int n, cons
 // Tiles are ordered per XCD: workgroup i runs on XCD i % 8, so XCD x takes a
 // contiguous range of tiles, activation tiles fastest, and the workgroups that
 // share a weight tile share that XCD's L2.
-constexpr int TL_BK = 32;                 // K per stage
-constexpr int TL_ROW = TL_BK * 2;         // bytes per row of a stage (4 chunks of 16 B)
+constexpr int TL_BK = 32;                 // K per stage of the default tiles
 
-// Byte offset of 16-byte chunk c (0..3) of row `row` in a stage region.  The
-// LDS serves 16 lanes (256 bytes, four 64-byte rows) per cycle; XOR-ing the
-// chunk with bits 2-3 of the row sends the 16 rows of one quarter of an MFMA
-// operand read to 16 distinct 16-byte bank groups.
-__device__ __forceinline__ int swz(int row, int c) { return row * TL_ROW + ((c ^ ((row >> 2) & 3)) << 4); }
+// Byte offset of 16-byte chunk c of row `row` in a stage region of BK-deep
+// rows (BK*2 bytes: 4 or 8 chunks).  The LDS serves 16 lanes (256 bytes) per
+// cycle; XOR-ing the chunk with the row's index among the rows that share a
+// 256-byte bank line's position (row / rows-per-256-bytes) sends the 16 rows of
+// one quarter of an MFMA operand read to 16 distinct 16-byte bank groups.
+template <int BK>
+__device__ __forceinline__ int swz(int row, int c) {
+  constexpr int ROW = BK * 2, CH = BK / 8, RP = 256 / ROW;
+  return row * ROW + ((c ^ ((row / RP) & (CH - 1))) << 4);
+}
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p));
@@ -111,60 +115,73 @@ __device__ __forceinline__ void wait_vm_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"i"(N) : "memory");
 }
 
-// Fragment reads of one 16-deep step: TN weight fragments at a + 2048 i and TM
-// activation fragments at b + 2048 j (consecutive 32-row blocks), each one
-// ds_read_b128 per lane; the asm waits for its reads before returning.
-template <int TN, int TM>
+// Fragment reads of one 16-deep step: TN weight fragments at a + D i and TM
+// activation fragments at b + D j (consecutive 32-row blocks, D bytes apart),
+// each one ds_read_b128 per lane; the asm waits for its reads before returning.
+template <int TN, int TM, int D>
 __device__ __forceinline__ void lds_frags(uint32_t a, uint32_t b, u32x4 (&fa)[TN], u32x4 (&fb)[TM]);
 
-template <>
-__device__ __forceinline__ void lds_frags<2, 4>(uint32_t a, uint32_t b, u32x4 (&fa)[2], u32x4 (&fb)[4]) {
+template <int D>
+__device__ __forceinline__ void lds_frags_2_4(uint32_t a, uint32_t b, u32x4 (&fa)[2], u32x4 (&fb)[4]) {
   asm volatile(
       "ds_read_b128 %0, %6\n\t"
-      "ds_read_b128 %1, %6 offset:2048\n\t"
+      "ds_read_b128 %1, %6 offset:%8\n\t"
       "ds_read_b128 %2, %7\n\t"
-      "ds_read_b128 %3, %7 offset:2048\n\t"
-      "ds_read_b128 %4, %7 offset:4096\n\t"
-      "ds_read_b128 %5, %7 offset:6144\n\t"
+      "ds_read_b128 %3, %7 offset:%8\n\t"
+      "ds_read_b128 %4, %7 offset:%9\n\t"
+      "ds_read_b128 %5, %7 offset:%10\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(fa[0]), "=&v"(fa[1]), "=&v"(fb[0]), "=&v"(fb[1]), "=&v"(fb[2]), "=&v"(fb[3])
-      : "v"(a), "v"(b)
+      : "v"(a), "v"(b), "i"(D), "i"(2 * D), "i"(3 * D)
       : "memory");
 }
 
-template <>
-__device__ __forceinline__ void lds_frags<2, 2>(uint32_t a, uint32_t b, u32x4 (&fa)[2], u32x4 (&fb)[2]) {
+template <int D>
+__device__ __forceinline__ void lds_frags_2_2(uint32_t a, uint32_t b, u32x4 (&fa)[2], u32x4 (&fb)[2]) {
   asm volatile(
       "ds_read_b128 %0, %4\n\t"
-      "ds_read_b128 %1, %4 offset:2048\n\t"
+      "ds_read_b128 %1, %4 offset:%6\n\t"
       "ds_read_b128 %2, %5\n\t"
-      "ds_read_b128 %3, %5 offset:2048\n\t"
+      "ds_read_b128 %3, %5 offset:%6\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(fa[0]), "=&v"(fa[1]), "=&v"(fb[0]), "=&v"(fb[1])
-      : "v"(a), "v"(b)
+      : "v"(a), "v"(b), "i"(D)
       : "memory");
 }
 
-template <>
-__device__ __forceinline__ void lds_frags<1, 2>(uint32_t a, uint32_t b, u32x4 (&fa)[1], u32x4 (&fb)[2]) {
+template <int D>
+__device__ __forceinline__ void lds_frags_1_2(uint32_t a, uint32_t b, u32x4 (&fa)[1], u32x4 (&fb)[2]) {
   asm volatile(
       "ds_read_b128 %0, %3\n\t"
       "ds_read_b128 %1, %4\n\t"
-      "ds_read_b128 %2, %4 offset:2048\n\t"
+      "ds_read_b128 %2, %4 offset:%5\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(fa[0]), "=&v"(fb[0]), "=&v"(fb[1])
-      : "v"(a), "v"(b)
+      : "v"(a), "v"(b), "i"(D)
       : "memory");
 }
 
-template <int EPI, int BN, int BM, int WN, int WM, int NBUF>
+template <int TN, int TM, int D>
+__device__ __forceinline__ void lds_frags(uint32_t a, uint32_t b, u32x4 (&fa)[TN], u32x4 (&fb)[TM]) {
+  if constexpr (TN == 2 && TM == 4)
+    lds_frags_2_4<D>(a, b, fa, fb);
+  else if constexpr (TN == 2 && TM == 2)
+    lds_frags_2_2<D>(a, b, fa, fb);
+  else if constexpr (TN == 1 && TM == 2)
+    lds_frags_1_2<D>(a, b, fa, fb);
+  else
+    static_assert(TN < 0, "no fragment reader for this wavefront tile");
+}
+
+template <int EPI, int BN, int BM, int WN, int WM, int NBUF, int BK>
 __global__ void __launch_bounds__(WN * WM * 64) k_gemm_tiled(GemmArgs g) {
   constexpr int T = WN * WM * 64;
   constexpr int TN = BN / WN / 32, TM = BM / WM / 32;
-  constexpr int STAGE = (BN + BM) * TL_ROW;       // bytes per stage
+  constexpr int ROW = BK * 2, CH = BK / 8;         // bytes and 16-byte chunks per stage row
+  constexpr int STAGE = (BN + BM) * ROW;          // bytes per stage
   constexpr int BLK = STAGE / 1024 / (T / 64);    // 1-KB load blocks per wavefront per stage
   static_assert(STAGE % (1024 * (T / 64)) == 0, "stage must split into 1 KB blocks per wavefront");
-  static_assert(BN % 16 == 0, "a 1 KB block (16 rows) must not straddle the weight/activation regions");
+  static_assert(BN % (1024 / ROW) == 0, "a 1 KB block must not straddle the weight/activation regions");
   static_assert(NBUF >= 2 && NBUF <= 6, "wait ladder covers up to four later stages");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NBUF * STAGE];
 
@@ -183,15 +200,15 @@ __global__ void __launch_bounds__(WN * WM * 64) k_gemm_tiled(GemmArgs g) {
   const bf16_t* A = static_cast<const bf16_t*>(g.a);
   const bf16_t* W = static_cast<const bf16_t*>(g.w);
 
-  // Load block q = w*BLK + b of a stage is 16 rows x 64 bytes; lane l fills the
-  // 16-byte slot 64q + l, i.e. physical chunk l % 4 of row 16q' + l / 4 of its
-  // region, and so reads the logical chunk that the swizzle puts there.
+  // Load block q = w*BLK + b of a stage is 1 KB of whole rows; lane l fills the
+  // 16-byte slot 64q + l, i.e. a physical chunk of one row of its region, and so
+  // reads the logical chunk that the swizzle puts there.
   const bf16_t* src[BLK];
 #pragma unroll
   for (int b = 0; b < BLK; ++b) {
     const int slot = (w * BLK + b) * 64 + lane;
-    const int row = slot >> 2;
-    const int c = (slot & 3) ^ ((row >> 2) & 3);
+    const int row = slot / CH;
+    const int c = (slot % CH) ^ ((row / (256 / ROW)) & (CH - 1));
     if (row < BN) {
       src[b] = W + static_cast<size_t>(n0 + row) * g.K + c * 8;
     } else {
@@ -200,13 +217,13 @@ __global__ void __launch_bounds__(WN * WM * 64) k_gemm_tiled(GemmArgs g) {
     }
   }
   // this workgroup's stages: [k_lo, k_lo + nk) of the K / 32 stages
-  const int k_lo = split * (g.K / TL_BK) / S;
-  const int nk = (split + 1) * (g.K / TL_BK) / S - k_lo;
+  const int k_lo = split * (g.K / BK) / S;
+  const int nk = (split + 1) * (g.K / BK) / S - k_lo;
   auto issue = [&](int kt) {  // kt counts this workgroup's stages from 0
     uint8_t* dst = lds + (kt % NBUF) * STAGE + w * BLK * 1024;
 #pragma unroll
     for (int b = 0; b < BLK; ++b)
-      load_lds16(src[b] + (k_lo + kt) * TL_BK, dst + b * 1024);
+      load_lds16(src[b] + (k_lo + kt) * BK, dst + b * 1024);
   };
 
   f32x16 acc[TN][TM];
@@ -218,12 +235,15 @@ __global__ void __launch_bounds__(WN * WM * 64) k_gemm_tiled(GemmArgs g) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int arow = lane & 31, ahalf = lane >> 5;
-  // fragment offsets within a stage for the two 16-deep steps (chunk 2s + ahalf)
-  uint32_t fa_off[2], fb_off[2];
+  // fragment offsets within a stage for its 16-deep steps (chunk 2s + ahalf);
+  // the swizzle key repeats every 32 rows, so consecutive 32-row blocks sit
+  // 32 rows apart
+  constexpr int NSTEP = BK / 16;
+  uint32_t fa_off[NSTEP], fb_off[NSTEP];
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    fa_off[s] = swz(wn * TN * 32 + arow, 2 * s + ahalf);
-    fb_off[s] = BN * TL_ROW + swz(wm * TM * 32 + arow, 2 * s + ahalf);
+  for (int s = 0; s < NSTEP; ++s) {
+    fa_off[s] = swz<BK>(wn * TN * 32 + arow, 2 * s + ahalf);
+    fb_off[s] = BN * ROW + swz<BK>(wm * TM * 32 + arow, 2 * s + ahalf);
   }
   const uint32_t lbase = lds_addr(lds);
   // A wavefront whose activation rows all lie past the live rows (the ragged
@@ -251,9 +271,9 @@ __global__ void __launch_bounds__(WN * WM * 64) k_gemm_tiled(GemmArgs g) {
     if (!live) continue;
     const uint32_t sb = lbase + (kt % NBUF) * STAGE;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < NSTEP; ++s) {
       u32x4 fa[TN], fb[TM];
-      lds_frags<TN, TM>(sb + fa_off[s], sb + fb_off[s], fa, fb);
+      lds_frags<TN, TM, 32 * ROW>(sb + fa_off[s], sb + fb_off[s], fa, fb);
 #pragma unroll
       for (int i = 0; i < TN; ++i)
 #pragma unroll
@@ -412,12 +432,12 @@ size_t gemm_workspace_bytes(int M, int N, int K) {
   return S > 1 ? static_cast<size_t>(S) * M * N * sizeof(float) : 0;
 }
 
-template <int EPI, int BN, int BM, int WN, int WM, int NBUF>
+template <int EPI, int BN, int BM, int WN, int WM, int NBUF, int BK = TL_BK>
 static void launch_tiled(const GemmArgs& g, hipStream_t s) {
   const int S = EPI == EPI_SPLITK ? g.ksplit : 1;
   const int total = (g.N / BN) * S * ((g.M + BM - 1) / BM);
   const int per = (total + 7) / 8;
-  hipLaunchKernelGGL((k_gemm_tiled<EPI, BN, BM, WN, WM, NBUF>), dim3(8 * per), dim3(WN * WM * 64), 0, s, g);
+  hipLaunchKernelGGL((k_gemm_tiled<EPI, BN, BM, WN, WM, NBUF, BK>), dim3(8 * per), dim3(WN * WM * 64), 0, s, g);
 }
 
 template <int EPI>
@@ -431,24 +451,29 @@ static hipError_t launch_epi(const GemmArgs& g, hipStream_t s) {
     else if (g.M <= 128)
       launch_tiled<EPI, 256, 128, 4, 2, 3>(g, s);
     else
-      launch_tiled<EPI, 256, 256, 4, 2, 4>(g, s);
+      launch_tiled<EPI, 256, 256, 4, 2, 2, 64>(g, s);
   } else if (g.M <= SK_BM) {
     const int S = gemm_ksplit(g.M, g.N, g.K);
     if (S > 1) {
       if (!g.kpart) return hipErrorInvalidValue;
       GemmArgs h = g;
       h.ksplit = S;
-      launch_tiled<EPI_SPLITK, SK_BN, SK_BM, 4, 1, 6>(h, s);
+      launch_tiled<EPI_SPLITK, SK_BN, SK_BM, 4, 1, 3, 64>(h, s);
       const int cols = EPI == EPI_SWIGLU ? g.N / 2 : g.N;
       hipLaunchKernelGGL((k_splitk_reduce<EPI>), dim3((g.M * (cols / 4) + 255) / 256), dim3(256), 0, s, h);
     } else {
-      launch_tiled<EPI, SK_BN, SK_BM, 4, 1, 6>(g, s);
+      launch_tiled<EPI, SK_BN, SK_BM, 4, 1, 3, 64>(g, s);
     }
   } else {
     // 256 x 256 tiles where they still give at least one wave of workgroups
-    // (the SwiGLU gate/up projection); 128 x 128 otherwise
+    // (the SwiGLU gate/up projection); 128 x 128 otherwise: with at most one
+    // tile per CU (down, O projections at batch 32) one workgroup per CU with a
+    // deeper ring of 64-deep stages, else two per CU with 32-deep stages
+    const int t128 = (g.N / 128) * ((g.M + 127) / 128);
     if (g.N % 256 == 0 && (g.N / 256) * ((g.M + 255) / 256) >= 256)
-      launch_tiled<EPI, 256, 256, 4, 2, 4>(g, s);
+      launch_tiled<EPI, 256, 256, 4, 2, 2, 64>(g, s);
+    else if (t128 <= 256)
+      launch_tiled<EPI, 128, 128, 2, 2, 3, 64>(g, s);
     else
       launch_tiled<EPI, 128, 128, 2, 2, 4>(g, s);
   }
