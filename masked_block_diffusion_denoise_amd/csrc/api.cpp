@@ -187,9 +187,8 @@ dlm_status run_layers(const dlm_model* m, const dlm_kv* kv, const int32_t* token
   const int R = B * Lq;
   const int d = c.d_model, qd = c.n_heads * c.head_dim, nq = qkv_dim(c);
   DLM_TRY(embed_norm(tokens, R, Lq, tok_ld, m->embed, c.vocab, d, m->attn_norm[0], c.rms_eps, p.x, p.xn,
-                     flags ? flags + 1 : nullptr, s),
+                     flags ? flags + 1 : nullptr, prefix, pos_offset, c.head_dim, c.rope_base, p.tab, s),
           "embed_norm");
-  DLM_TRY(rope_table(prefix, pos_offset, B, Lq, c.head_dim, c.rope_base, p.tab, s), "rope_table");
   const size_t lkv = layer_kv_elems(c, kv);
   for (int l = 0; l < c.n_layers; ++l) {
     bf16_t* kc = static_cast<bf16_t*>(kv->k) + l * lkv;
@@ -269,12 +268,13 @@ dlm_status run_layers(const dlm_model* m, const dlm_kv* kv, const int32_t* token
   return DLM_OK;
 }
 
-// Final norm of the selected rows (all R if rows == null) and the fused head.
+// Final norm of the selected rows (all R if rows == null; skipped when the
+// caller already normalised them into p.xn) and the fused head.
 dlm_status run_head(const dlm_model* m, int R, const int* rows, const int* count, const int* out_rows, float* conf,
                     int32_t* argmax, float* logits, int32_t* flags, const PassBufs& p, hipStream_t s,
-                    bool time_head) {
+                    bool time_head, bool norm = true) {
   const dlm_config& c = m->c;
-  DLM_TRY(rmsnorm(p.x, R, c.d_model, m->final_norm, c.rms_eps, p.xn, rows, count, s), "final norm");
+  if (norm) DLM_TRY(rmsnorm(p.x, R, c.d_model, m->final_norm, c.rms_eps, p.xn, rows, count, s), "final norm");
   GemmArgs g{};
   g.a = p.xn;
   g.w = m->lm_head;
@@ -465,8 +465,9 @@ dlm_status dlm_denoise_step(const dlm_model* m, const dlm_kv* kv, const int32_t*
   hipStream_t s = static_cast<hipStream_t>(stream);
   const PassBufs p = carve(m->c, reinterpret_cast<uintptr_t>(ws), R, B, L, max_kv, false);
   if ((st = run_layers(m, kv, canvas, L, B, L, prefix_len, 0, 0, max_kv, flags, p, s)) != DLM_OK) return st;
-  DLM_TRY(masked_rows(masked, R, p.rows, p.count, s), "masked rows");
-  return run_head(m, R, p.rows, p.count, p.rows, conf, argmax, logits, flags, p, s, true);
+  DLM_TRY(masked_norm(masked, R, p.x, m->c.d_model, m->final_norm, m->c.rms_eps, p.xn, p.rows, p.count, s),
+          "masked rows + final norm");
+  return run_head(m, R, p.rows, p.count, p.rows, conf, argmax, logits, flags, p, s, true, false);
 }
 
 dlm_status dlm_commit(const float* conf, const int32_t* argmax, int32_t* canvas, uint8_t* masked, int32_t B,

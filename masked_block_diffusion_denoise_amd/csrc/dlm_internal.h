@@ -70,16 +70,21 @@ hipError_t attention(const AttnArgs& a, hipStream_t s);
 hipError_t commit(const float* conf, const int* argmax, int* canvas, uint8_t* masked, int B, int L,
                   const float* tau, const int* quota, int* steps, int max_steps, int* n_committed,
                   int* n_left, hipStream_t s);
-// row m = b*Lq + j takes token tokens[b*tok_ld + j]
+// row m = b*Lq + j takes token tokens[b*tok_ld + j]; with tab, the same launch
+// fills the RoPE table of the pass (rope_table's layout)
 hipError_t embed_norm(const int* tokens, int M, int Lq, int tok_ld, const void* embed, int V, int d,
-                      const void* gain, float eps, float* x, void* xn, int* bad_token, hipStream_t s);
+                      const void* gain, float eps, float* x, void* xn, int* bad_token, const int* prefix,
+                      int pos_offset, int hd, float base, float2* tab, hipStream_t s);
 hipError_t rmsnorm(const float* x, int M, int d, const void* gain, float eps, void* xn,
                    const int* rows, const int* m_dev, hipStream_t s);
 hipError_t rope_table(const int* prefix, int pos_offset, int B, int Lq, int hd, float base, float2* tab,
                       hipStream_t s);
 hipError_t rope_kv(void* qkv, int M, int Lq, int H, int G, int hd, const float2* tab, void* kc, void* vc,
                    const int* prefix, int pos_offset, int cap, hipStream_t s);
-hipError_t masked_rows(const uint8_t* masked, int M, int* rows, int* count, hipStream_t s);
+// rows[0..count) = indices m with masked[m] != 0, ascending, and count[0] = how
+// many, fused with the final RMSNorm of those rows into xn[0..count)
+hipError_t masked_norm(const uint8_t* masked, int M, const float* x, int d, const void* gain, float eps, void* xn,
+                       int* rows, int* count, hipStream_t s);
 hipError_t head_merge(const void* partials, int n_tiles, int M, const int* rows, const int* m_dev,
                       float* conf, int* argmax, int total_rows, hipStream_t s);
 hipError_t fill_i32(int* p, int n, int v, hipStream_t s);

@@ -487,6 +487,7 @@ hipError_t gemm(const GemmArgs& g, GemmEpilogue epi, hipStream_t s) {
     case EPI_RESID_F32: return launch_epi<EPI_RESID_F32>(g, s);
     case EPI_SWIGLU: return launch_epi<EPI_SWIGLU>(g, s);
     case EPI_HEAD: return launch_epi<EPI_HEAD>(g, s);
+    case EPI_SPLITK: break;
   }
   return hipErrorInvalidValue;
 }

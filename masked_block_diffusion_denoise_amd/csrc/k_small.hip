@@ -1,6 +1,6 @@
-// Small kernels of the denoising path: commit/remask, embedding gather + RMSNorm,
-// RMSNorm, RoPE table and RoPE + KV-cache write, masked-row compaction, the
-// cross-tile merge of the LM-head partials, and fills.
+// Small kernels of the denoising path: commit/remask, embedding gather + RMSNorm
+// (+ the RoPE table), RMSNorm, RoPE + KV-cache write, masked-row compaction +
+// final RMSNorm, the cross-tile merge of the LM-head partials, and fills.
 #include "dlm_device.h"
 #include "dlm_internal.h"
 
@@ -87,15 +87,44 @@ __device__ __forceinline__ void unpack8(u32x4 v, float* f) {
   }
 }
 
-// x[m] = E[tok[m]] (fp32) and xn[m] = RMSNorm(x[m]) * g (bf16).  RMSNorm is
-// x / sqrt(mean(x^2) + eps) * g.  Out-of-range tokens read as zeros and are counted.
-__global__ void __launch_bounds__(256) k_embed_norm(const int* __restrict__ tokens, int Lq, int tok_ld,
+// Rotation angles for row m = b*Lq + j at absolute position p = prefix[b] + off + j:
+// pair i of a head (components i and i + hd/2) turns by p * base^(-2i/hd).  The
+// angle is formed in double precision (positions reach 1e5 and beyond), its
+// cosine and sine are stored as fp32 and shared by every head and layer.
+struct RopeSpec {
+  const int* prefix;
+  int off, Lq, half;
+  double log_base;
+  float2* tab;
+  int total;  // rows * half entries (0: no table)
+};
+
+__device__ __forceinline__ void rope_entry(const RopeSpec& r, int e) {
+  const int m = e / r.half, i = e % r.half;
+  const int b = m / r.Lq, j = m % r.Lq;
+  const double p = static_cast<double>((r.prefix ? r.prefix[b] : 0) + r.off + j);
+  const double freq = exp(-2.0 * i / (2.0 * r.half) * r.log_base);
+  double sn, cs;
+  sincos(p * freq, &sn, &cs);
+  r.tab[e] = make_float2(static_cast<float>(cs), static_cast<float>(sn));
+}
+
+// Blocks [0, M): x[m] = E[tok[m]] (fp32) and xn[m] = RMSNorm(x[m]) * g (bf16),
+// RMSNorm being x / sqrt(mean(x^2) + eps) * g; out-of-range tokens read as
+// zeros and are counted.  Blocks past M fill the RoPE table of the pass (one
+// launch for both).
+__global__ void __launch_bounds__(256) k_embed_norm(const int* __restrict__ tokens, int M, int Lq, int tok_ld,
                                                     const bf16_t* __restrict__ E, int V, int d,
                                                     const bf16_t* __restrict__ g, float eps,
                                                     float* __restrict__ x, bf16_t* __restrict__ xn,
-                                                    int* __restrict__ bad) {
+                                                    int* __restrict__ bad, RopeSpec rope) {
   __shared__ float red[4];
   const int m = blockIdx.x;
+  if (m >= M) {
+    const int e = (m - M) * 256 + threadIdx.x;
+    if (e < rope.total) rope_entry(rope, e);
+    return;
+  }
   const int t = tokens[static_cast<size_t>(m / Lq) * tok_ld + m % Lq];
   const bool ok = t >= 0 && t < V;
   if (!ok && threadIdx.x == 0 && bad) atomicAdd(bad, 1);
@@ -126,10 +155,14 @@ __global__ void __launch_bounds__(256) k_embed_norm(const int* __restrict__ toke
 }
 
 hipError_t embed_norm(const int* tokens, int M, int Lq, int tok_ld, const void* embed, int V, int d,
-                      const void* gain, float eps, float* x, void* xn, int* bad_token, hipStream_t s) {
+                      const void* gain, float eps, float* x, void* xn, int* bad_token, const int* prefix,
+                      int pos_offset, int hd, float base, float2* tab, hipStream_t s) {
   if (M <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_embed_norm, dim3(M), dim3(256), 0, s, tokens, Lq, tok_ld, static_cast<const bf16_t*>(embed), V,
-                     d, static_cast<const bf16_t*>(gain), eps, x, static_cast<bf16_t*>(xn), bad_token);
+  RopeSpec r{prefix, pos_offset, Lq, hd / 2, log(static_cast<double>(base)), tab, tab ? M * (hd / 2) : 0};
+  const int tab_blocks = (r.total + 255) / 256;
+  hipLaunchKernelGGL(k_embed_norm, dim3(M + tab_blocks), dim3(256), 0, s, tokens, M, Lq, tok_ld,
+                     static_cast<const bf16_t*>(embed), V, d, static_cast<const bf16_t*>(gain), eps, x,
+                     static_cast<bf16_t*>(xn), bad_token, r);
   return hipGetLastError();
 }
 
@@ -172,29 +205,16 @@ hipError_t rmsnorm(const float* x, int M, int d, const void* gain, float eps, vo
 }
 
 // ---------------------------------------------------------------- RoPE ----
-// Rotation angles for row m = b*Lq + j at absolute position p = prefix[b] + off + j:
-// pair i of a head (components i and i + hd/2) turns by p * base^(-2i/hd).  The
-// angle is formed in double precision (positions reach 1e5 and beyond), its
-// cosine and sine are stored as fp32 and shared by every head and layer.
-__global__ void k_rope_table(const int* __restrict__ prefix, int off, int Lq, int half, double log_base,
-                             float2* __restrict__ tab, int total) {
+__global__ void k_rope_table(RopeSpec r) {
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= total) return;
-  const int m = e / half, i = e % half;
-  const int b = m / Lq, j = m % Lq;
-  const double p = static_cast<double>((prefix ? prefix[b] : 0) + off + j);
-  const double freq = exp(-2.0 * i / (2.0 * half) * log_base);
-  double sn, cs;
-  sincos(p * freq, &sn, &cs);
-  tab[e] = make_float2(static_cast<float>(cs), static_cast<float>(sn));
+  if (e < r.total) rope_entry(r, e);
 }
 
 hipError_t rope_table(const int* prefix, int pos_offset, int B, int Lq, int hd, float base, float2* tab,
                       hipStream_t s) {
-  const int total = B * Lq * (hd / 2);
-  if (total <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_rope_table, dim3((total + 255) / 256), dim3(256), 0, s, prefix, pos_offset, Lq, hd / 2,
-                     log(static_cast<double>(base)), tab, total);
+  RopeSpec r{prefix, pos_offset, Lq, hd / 2, log(static_cast<double>(base)), tab, B * Lq * (hd / 2)};
+  if (r.total <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_rope_table, dim3((r.total + 255) / 256), dim3(256), 0, s, r);
   return hipGetLastError();
 }
 
@@ -264,37 +284,50 @@ hipError_t rope_kv(void* qkv, int M, int Lq, int H, int G, int hd, const float2*
 }
 
 // ------------------------------------------------------ masked rows ----
-// rows[0..count) = indices m with masked[m] != 0, ascending; count[0] = how many.
-__global__ void __launch_bounds__(1024) k_masked_rows(const uint8_t* __restrict__ masked, int M,
-                                                      int* __restrict__ rows, int* __restrict__ count) {
-  __shared__ int wsum[16];
-  __shared__ int carry;
-  if (threadIdx.x == 0) carry = 0;
-  __syncthreads();
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  for (int base = 0; base < M; base += 1024) {
-    const int m = base + threadIdx.x;
-    const int f = (m < M && masked[m]) ? 1 : 0;
-    const unsigned long long bal = __ballot(f);
-    const int before = __popcll(bal & ((1ull << lane) - 1ull));
-    if (lane == 0) wsum[w] = __popcll(bal);
-    __syncthreads();
-    int off = carry;
-    for (int i = 0; i < w; ++i) off += wsum[i];
-    if (f) rows[off + before] = m;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      int t = 0;
-      for (int i = 0; i < 16; ++i) t += wsum[i];
-      carry += t;
-    }
-    __syncthreads();
+// Masked-row compaction fused with the final RMSNorm: block m (one per canvas
+// row) counts the masked rows before it; a masked row goes to slot `idx` of the
+// compacted list (rows[idx] = m, xn[idx] = RMSNorm(x[m]) * g) and the last block
+// writes the count.  Rows keep their canvas order.
+__global__ void __launch_bounds__(256) k_masked_norm(const uint8_t* __restrict__ masked, int M,
+                                                     const float* __restrict__ x, int d,
+                                                     const bf16_t* __restrict__ g, float eps,
+                                                     bf16_t* __restrict__ xn, int* __restrict__ rows,
+                                                     int* __restrict__ count) {
+  __shared__ float red[4];
+  const int m = blockIdx.x;
+  float before = 0.f;
+  for (int i = threadIdx.x; i < m; i += 256) before += masked[i] ? 1.f : 0.f;
+  const int idx = static_cast<int>(block_sum_256(before, red));  // exact: at most M < 2^24
+  const bool mine = masked[m] != 0;
+  if (m == M - 1 && threadIdx.x == 0) count[0] = idx + (mine ? 1 : 0);
+  if (!mine) return;
+  if (threadIdx.x == 0) rows[idx] = m;
+  const float* xr = x + static_cast<size_t>(m) * d;
+  float ss = 0.f;
+  for (int c = threadIdx.x; c < d / 4; c += 256) {
+    const float4 v = reinterpret_cast<const float4*>(xr)[c];
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
   }
-  if (threadIdx.x == 0) count[0] = carry;
+  const float rstd = rsqrtf(block_sum_256(ss, red) / d + eps);
+  for (int c = threadIdx.x; c < d / 8; c += 256) {
+    const float4 v0 = reinterpret_cast<const float4*>(xr)[2 * c];
+    const float4 v1 = reinterpret_cast<const float4*>(xr)[2 * c + 1];
+    float gg[8];
+    unpack8(ld16(g + c * 8), gg);
+    u32x4 o;
+    o[0] = pack_bf16x2(v0.x * rstd * gg[0], v0.y * rstd * gg[1]);
+    o[1] = pack_bf16x2(v0.z * rstd * gg[2], v0.w * rstd * gg[3]);
+    o[2] = pack_bf16x2(v1.x * rstd * gg[4], v1.y * rstd * gg[5]);
+    o[3] = pack_bf16x2(v1.z * rstd * gg[6], v1.w * rstd * gg[7]);
+    st16(xn + static_cast<size_t>(idx) * d + c * 8, o);
+  }
 }
 
-hipError_t masked_rows(const uint8_t* masked, int M, int* rows, int* count, hipStream_t s) {
-  hipLaunchKernelGGL(k_masked_rows, dim3(1), dim3(1024), 0, s, masked, M, rows, count);
+hipError_t masked_norm(const uint8_t* masked, int M, const float* x, int d, const void* gain, float eps, void* xn,
+                       int* rows, int* count, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_masked_norm, dim3(M), dim3(256), 0, s, masked, M, x, d, static_cast<const bf16_t*>(gain), eps,
+                     static_cast<bf16_t*>(xn), rows, count);
   return hipGetLastError();
 }
 

@@ -201,3 +201,39 @@ def test_layer8b_denoise_step(layer8b, B, rows):
                 fin = np.isfinite(lo[j])
                 assert rel_rms(lg_all[b, j][fin], lo[j][fin]) < 2e-2
     assert (host(sess.flags) == 0).all()
+
+
+def test_layer8b_append_block_batch1(layer8b):
+    # batch 1 runs the K-split projections whose partial sums fold into RoPE + KV
+    # write and into the residual add + norm: the appended keys/values and the
+    # causal next-token predictions must match the oracle's causal pass
+    announce("8B layer append B=1")
+    shape, w, m = layer8b
+    B, P, Lb = 1, 4096, 32
+    k, v = synth.kv_prefix(shape, B, P, seed=5)
+    block = synth.prompt(shape, B, Lb, seed=5)
+    sess = R.Session(m, B, P + Lb + 64, Lb)
+    sess.kv.write(0, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda())
+    sess.prefix.fill_(P)
+    sess.max_prefix = P
+    sess.canvas.copy_(i32(block))
+    arg = torch.zeros(B, Lb, dtype=torch.int32, device="cuda")
+    conf = torch.zeros(B, Lb, dtype=torch.float32, device="cuda")
+    sess.append_block(arg, conf)
+    sync()
+    cache = oracle.KVCache(shape)
+    cache.k[0] = k[0].astype(np.float64)
+    cache.v[0] = v[0].astype(np.float64)
+    x = oracle.append_block(w, shape, cache, block[0])
+    kg = host(sess.kv.k_logical()[0, 0, :, P:P + Lb].float())
+    vg = host(sess.kv.v_logical()[0, 0, :, P:P + Lb].float())
+    assert rel_rms(kg, cache.k[0][:, P:P + Lb]) < 1e-2
+    assert rel_rms(vg, cache.v[0][:, P:P + Lb]) < 1e-2
+    assert int(host(sess.prefix)[0]) == P + Lb
+    lo = oracle.head_logits(w, shape, x)
+    conf_o, arg_o = oracle.confidence(lo)
+    assert np.abs(host(conf)[0] - conf_o).max() < 1e-2
+    for j in range(Lb):
+        top2 = np.sort(lo[j][np.isfinite(lo[j])])[-2:]
+        if top2[1] - top2[0] > 5e-2:
+            assert host(arg)[0, j] == arg_o[j], j
