@@ -9,8 +9,9 @@ library (the two share only the seeded input generators in ``synth``).
 Sources (web pages this follows; cited by title and section):
   [MLX guide]   "MLX-VLM: running NVIDIA Nemotron Labs Diffusion -- AR, block
                 diffusion and linear self-speculation decoding" (xxqk.cn):
-                sec. 5.2 samplers, 5.3 head scoring, 6 masked block denoising,
-                7 architecture, 8 linear self-speculation, 9 statistics.
+                sec. 3.3 LoRA adapter, 5.2 samplers, 5.3 head scoring, 6 masked
+                block denoising, 7 architecture, 8 linear self-speculation,
+                9 statistics.
   [NLD tutorial] "NVlabs/Nemotron-Labs-Diffusion -- Tri-Mode diffusion LM
                 tutorial": sec. 3.1 (one set of weights, three decoding loops).
   [DiffusionGemma] diffusers "DiffusionGemma" pipeline docs: Schedulers
@@ -29,6 +30,9 @@ Pins (what each function is checked against, in tests/test_oracle_*.py):
                              quota 1 takes L steps; all-confident takes 1),
                              never-remask, forced completion, worked example A
   generate_ar                equals recompute-from-scratch causal argmax decoding
+  generate_linear_spec       equals generate_ar token for token (lossless), with
+                             and without the adaptive window; its trimmed cache
+                             equals a causal prefill of prompt + output
 Whole-model numeric values of a random-init network are not printed on any
 page: beyond the pins above, those are "parity unpinned" (self-consistency only).
 """
@@ -36,11 +40,13 @@ from .model import (KVCache, rms_norm, rope, attend, forward, head_logits,
                     confidence, silu)
 from .decode import (commit, commit_batch, linear_mask_schedule, sample_fixed_schedule,
                      generate_block_diffusion, generate_ar, generate_ar_recompute,
-                     denoise_logits, append_block, prefill, BlockStats)
+                     denoise_logits, append_block, prefill, BlockStats,
+                     generate_linear_spec, next_draft_window)
 
 __all__ = [
     "KVCache", "rms_norm", "rope", "attend", "forward", "head_logits", "confidence",
     "silu", "commit", "commit_batch", "linear_mask_schedule", "sample_fixed_schedule",
     "generate_block_diffusion", "generate_ar", "generate_ar_recompute",
     "denoise_logits", "append_block", "prefill", "BlockStats",
+    "generate_linear_spec", "next_draft_window",
 ]

@@ -113,9 +113,9 @@ def prefill(w, shape, prompt):
     return cache, x
 
 
-def denoise_logits(w, shape, cache, canvas):
+def denoise_logits(w, shape, cache, canvas, lora=None):
     """One bidirectional-block pass of the canvas against the cached prefix; no cache write."""
-    x = forward(w, shape, canvas, cache, mode="block", write_cache=False)
+    x = forward(w, shape, canvas, cache, mode="block", write_cache=False, lora=lora)
     return head_logits(w, shape, x)
 
 
@@ -199,3 +199,58 @@ def generate_ar_recompute(w, shape, prompt, n_new):
         out.append(int(arg[0]))
         seq.append(int(arg[0]))
     return np.array(out, dtype=np.int64)
+
+
+# ------------------------------------------------------------ linear self-speculation
+def next_draft_window(window, accepted, max_window=32, min_window=2):
+    """Adaptive draft window of linear self-speculation (MLX guide, sec. 8): it
+    starts at 8, doubles (up to 32) when a round accepts every draft token, and
+    halves when at most half of them are accepted.  ``window`` counts the known
+    token plus window - 1 drafted positions; the floor of 2 keeps one drafted
+    position (a reading: the page gives no lower bound)."""
+    drafts = window - 1
+    if accepted == drafts:
+        return min(window * 2, max_window)
+    if accepted * 2 <= drafts:
+        return max(window // 2, min_window)
+    return window
+
+
+def generate_linear_spec(w, shape, prompt, n_new, lora, window=32, adaptive=False):
+    """Linear self-speculation, greedy (MLX guide, sec. 8; NLD tutorial, sec. 3.1).
+
+    Each round drafts a block with one bidirectional pass of the canvas
+    [t, MASK x (W - 1)] -- t is the next token, already known -- with the LoRA
+    adapter on, taking the argmax of every masked position.  A causal pass over
+    [t, drafts] with the adapter off then verifies them: the longest prefix of
+    drafts equal to the causal argmax is accepted, and the causal argmax after it
+    is the next known token (the correction).  The cache is trimmed back to the
+    known token and the accepted drafts.  Every emitted token is the greedy
+    causal prediction of its prefix, so the output equals ``generate_ar``.
+
+    Returns (tokens [n_new], accepted drafts per round, windows per round, cache).
+    """
+    cache, x = prefill(w, shape, prompt)
+    _, arg = confidence(head_logits(w, shape, x[-1:]))
+    nxt = int(arg[0])
+    out, accepted, windows = [], [], []
+    W = 8 if adaptive else window
+    while len(out) < n_new:
+        p0 = cache.length
+        canvas = np.array([nxt] + [shape.mask_id] * (W - 1), dtype=np.int64)
+        _, drafts = confidence(denoise_logits(w, shape, cache, canvas, lora=lora))
+        drafts = drafts[1:]
+        block = np.concatenate([[nxt], drafts])
+        xv = append_block(w, shape, cache, block)
+        _, ver = confidence(head_logits(w, shape, xv))   # ver[j]: causal argmax after block[j]
+        a = 0
+        while a < W - 1 and drafts[a] == ver[a]:
+            a += 1
+        out.extend(block[:a + 1].tolist())
+        nxt = int(ver[a])
+        cache.truncate(p0 + a + 1)
+        accepted.append(a)
+        windows.append(W)
+        if adaptive:
+            W = next_draft_window(W, a)
+    return np.array(out[:n_new], dtype=np.int64), accepted, windows, cache

@@ -118,7 +118,7 @@ def _mask_for(mode, positions, n_prefix):
 
 
 def forward(w, shape, tokens, cache=None, mode="causal", write_cache=False,
-            positions=None):
+            positions=None, lora=None):
     """Run the decoder stack over ``tokens`` placed after the cached prefix.
 
     Returns the final residual stream [T, d] (before the final norm).  With
@@ -126,6 +126,11 @@ def forward(w, shape, tokens, cache=None, mode="causal", write_cache=False,
     pass never writes (its keys/values were computed from a masked canvas and
     may not enter the history; Module 12, sec. 14).  ``mode`` is "causal",
     "block" or an explicit boolean mask [T, P + T].
+
+    ``lora`` (optional): {"a": per-layer [r, H*hd], "b": per-layer [d, r],
+    "scale": s} adds s * (o A^T) B^T to every layer's output projection -- the
+    draft-only adapter of linear self-speculation (MLX guide, sec. 3.3 and 8:
+    rank 128, scale 4.0, on self_attn.o_proj only).
     """
     tokens = np.asarray(tokens, dtype=np.int64)
     t = tokens.shape[0]
@@ -150,6 +155,9 @@ def forward(w, shape, tokens, cache=None, mode="causal", write_cache=False,
             kk, vv = k, v
         o = attend(q, kk, vv, allowed).transpose(1, 0, 2).reshape(t, h_ * hd)
         x = x + o @ np.asarray(lw["wo"], F64).T
+        if lora is not None:
+            a_, b_ = np.asarray(lora["a"][li], F64), np.asarray(lora["b"][li], F64)
+            x = x + lora["scale"] * ((o @ a_.T) @ b_.T)
         n2 = rms_norm(x, lw["ffn_norm"], shape.rms_eps)
         gate = n2 @ np.asarray(lw["wg"], F64).T
         up = n2 @ np.asarray(lw["wu"], F64).T

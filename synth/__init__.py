@@ -129,6 +129,18 @@ def model_weights(shape: ModelShape, seed: int = 0, std: float = 0.02,
     return w
 
 
+def lora_weights(shape: ModelShape, rank: int = 128, scale: float = 4.0, seed: int = 0,
+                 std: float = 0.02) -> dict:
+    """Random-init low-rank adapter for every layer's output projection:
+    a [rank, H*hd] and b [d, rank], N(0, std) from their own seeded streams."""
+    a, b = [], []
+    for i in range(shape.n_layers):
+        s = 16 + 16 * i
+        a.append(normal(seed, K_WEIGHTS, (rank, shape.q_dim), std, s + 7))
+        b.append(normal(seed, K_WEIGHTS, (shape.d_model, rank), std, s + 8))
+    return {"a": a, "b": b, "scale": float(scale)}
+
+
 def prompt(shape: ModelShape, batch: int, length: int, seed: int = 0) -> np.ndarray:
     """Uniform random token ids over [0, V) without the mask id, int32 [B, T]."""
     g = rng(seed, K_PROMPT)
