@@ -110,6 +110,23 @@ typedef struct dlm_model dlm_model; /* opaque, host-side */
 dlm_status dlm_model_create(const dlm_config* cfg, const dlm_weights* w, dlm_model** out);
 void dlm_model_destroy(dlm_model* m);
 
+/* Low-rank adapter on every layer's attention output projection, used by the
+ * draft passes of linear self-speculation (MLX guide, sec. 3.3: rank 128,
+ * scale 4.0, on self_attn.o_proj only; sec. 8: enabled while drafting, disabled
+ * for the causal verification).  While enabled, every pass computes
+ *   o_proj(y) = y Wo^T + scale * (y A^T) B^T
+ *   a, b   [host] arrays of n_layers [dev] pointers (16-byte aligned), borrowed
+ *          like the weights: A bf16 [rank][n_heads*head_dim], B bf16 [d_model][rank]
+ *   rank   a multiple of 128, at most DLM_MAX_LORA_RANK
+ * a == b == NULL removes the adapter.  Setting an adapter leaves it disabled.
+ * The switch is host state of the handle: calls that overlap with it (on any
+ * thread) see either setting.  Errors: INVALID_ARG for NULL or misaligned
+ * matrices, a non-finite scale, or enabling with no adapter set; UNSUPPORTED
+ * for another rank. */
+#define DLM_MAX_LORA_RANK 256
+dlm_status dlm_model_set_lora(dlm_model* m, const void* const* a, const void* const* b, int32_t rank, float scale);
+dlm_status dlm_model_enable_lora(dlm_model* m, int32_t on);
+
 /* Bytes of workspace that a pass over up to `max_rows` rows (batch x tokens per
  * pass) against at most `max_kv` keys per row needs.  Enough for
  * dlm_denoise_step and dlm_append_block with B*L <= max_rows and

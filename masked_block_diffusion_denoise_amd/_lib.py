@@ -20,7 +20,8 @@ TIMER_LM_HEAD, TIMER_ATTENTION, TIMER_GATE_UP, TIMER_DOWN, TIMER_QKV = 0, 1, 2, 
 
 # Every function declared in include/libdlm.h and include/libdlm_ops.h.
 EXPORTS = [
-    "dlm_model_create", "dlm_model_destroy", "dlm_workspace_bytes", "dlm_prefill", "dlm_denoise_step",
+    "dlm_model_create", "dlm_model_destroy", "dlm_model_set_lora", "dlm_model_enable_lora",
+    "dlm_workspace_bytes", "dlm_prefill", "dlm_denoise_step",
     "dlm_commit", "dlm_append_block", "dlm_status_string", "dlm_last_error", "dlm_set_kernel_timer",
     "dlm_op_gemm_workspace_bytes", "dlm_op_gemm", "dlm_op_rmsnorm", "dlm_op_rope_workspace_bytes",
     "dlm_op_rope_kv", "dlm_op_attention_workspace_bytes", "dlm_op_attention",
@@ -59,6 +60,8 @@ vp, i32, f32, sz = C.c_void_p, C.c_int32, C.c_float, C.c_size_t
 _SIGS = {
     "dlm_model_create": (i32, [C.POINTER(Config), C.POINTER(Weights), C.POINTER(vp)]),
     "dlm_model_destroy": (None, [vp]),
+    "dlm_model_set_lora": (i32, [vp, C.POINTER(vp), C.POINTER(vp), i32, f32]),
+    "dlm_model_enable_lora": (i32, [vp, i32]),
     "dlm_workspace_bytes": (sz, [vp, i32, i32]),
     "dlm_prefill": (i32, [vp, C.POINTER(KV), vp, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
     "dlm_denoise_step": (i32, [vp, C.POINTER(KV), vp, i32, vp, vp, i32, i32, vp, vp, vp, vp, vp, sz, vp]),

@@ -22,6 +22,11 @@ struct dlm_model {
   const void* final_norm;
   const void* lm_head;
   std::vector<const void*> attn_norm, wqkv, wo, ffn_norm, wgu, wdown;
+  // optional low-rank adapter on the output projection (dlm_model_set_lora)
+  std::vector<const void*> lora_a, lora_b;
+  int lora_rank = 0;
+  float lora_scale = 0.f;
+  bool lora_on = false;
 };
 
 namespace {
@@ -96,6 +101,7 @@ struct PassBufs {
   int* count;
   float4* head_part;
   float* kpart;  // K-split partials of the layer projections (short passes only)
+  bf16_t* lora_t;  // [R][DLM_MAX_LORA_RANK] adapter activations (o A^T)
   size_t bytes;
 };
 
@@ -134,6 +140,10 @@ size_t layer_gemm_ws(const dlm_config& c, int R) {
     b = std::max(b, gemm_workspace_bytes(r, d, qd));
     b = std::max(b, gemm_workspace_bytes(r, 2 * c.d_ffn, d));
     b = std::max(b, gemm_workspace_bytes(r, d, c.d_ffn));
+    for (int rank = 128; rank <= DLM_MAX_LORA_RANK; rank += 128) {  // adapter: o A^T, then (.) B^T
+      b = std::max(b, gemm_workspace_bytes(r, rank, qd));
+      b = std::max(b, gemm_workspace_bytes(r, d, rank));
+    }
   }
   return b;
 }
@@ -155,6 +165,7 @@ PassBufs carve(const dlm_config& c, uintptr_t base, int R, int B, int Lq, int ma
   p.count = cv.take<int>(1);
   p.head_part = cv.take<float4>(head_part_records(c, R, bound));
   p.kpart = cv.take<float>(layer_gemm_ws(c, R) / sizeof(float));
+  p.lora_t = cv.take<bf16_t>(static_cast<size_t>(R) * DLM_MAX_LORA_RANK);
   p.bytes = align256(cv.off);
   return p;
 }
@@ -241,6 +252,28 @@ dlm_status run_layers(const dlm_model* m, const dlm_kv* kv, const int32_t* token
     g.lda = qd;
     g.ldc = d;
     DLM_TRY(gemm(g, EPI_RESID_F32, s), "gemm o");
+    if (m->lora_on) {  // x += scale * (o A^T) B^T
+      GemmArgs la{};
+      la.kpart = p.kpart;
+      la.a = p.attn;
+      la.w = m->lora_a[l];
+      la.out = p.lora_t;
+      la.M = R;
+      la.N = m->lora_rank;
+      la.K = qd;
+      la.lda = qd;
+      la.ldc = m->lora_rank;
+      DLM_TRY(gemm(la, EPI_STORE_BF16, s), "gemm lora a");
+      la.a = p.lora_t;
+      la.w = m->lora_b[l];
+      la.out = p.x;
+      la.N = d;
+      la.K = m->lora_rank;
+      la.lda = m->lora_rank;
+      la.ldc = d;
+      la.alpha = m->lora_scale;
+      DLM_TRY(gemm(la, EPI_RESID_F32, s), "gemm lora b");
+    }
     DLM_TRY(rmsnorm(p.x, R, d, m->ffn_norm[l], c.rms_eps, p.xn, nullptr, nullptr, s), "rmsnorm");
     g.a = p.xn;
     g.w = m->wgu[l];
@@ -370,6 +403,39 @@ dlm_status dlm_model_create(const dlm_config* cfg, const dlm_weights* w, dlm_mod
 }
 
 void dlm_model_destroy(dlm_model* m) { delete m; }
+
+dlm_status dlm_model_set_lora(dlm_model* m, const void* const* a, const void* const* b, int32_t rank, float scale) {
+  g_err[0] = 0;
+  if (!m) return fail(DLM_ERR_INVALID_ARG, "model is NULL");
+  if (!a && !b) {
+    m->lora_a.clear();
+    m->lora_b.clear();
+    m->lora_rank = 0;
+    m->lora_on = false;
+    return DLM_OK;
+  }
+  if (!a || !b) return fail(DLM_ERR_INVALID_ARG, "adapter needs both A and B pointer arrays");
+  if (rank < 128 || rank > DLM_MAX_LORA_RANK || rank % 128)
+    return fail(DLM_ERR_UNSUPPORTED, "adapter rank %d must be a multiple of 128 up to %d", rank, DLM_MAX_LORA_RANK);
+  if (!std::isfinite(scale)) return fail(DLM_ERR_INVALID_ARG, "adapter scale must be finite");
+  for (int l = 0; l < m->c.n_layers; ++l)
+    if (!a[l] || !b[l] || !aligned16(a[l]) || !aligned16(b[l]))
+      return fail(DLM_ERR_INVALID_ARG, "adapter matrices of layer %d NULL or not 16-byte aligned", l);
+  m->lora_a.assign(a, a + m->c.n_layers);
+  m->lora_b.assign(b, b + m->c.n_layers);
+  m->lora_rank = rank;
+  m->lora_scale = scale;
+  m->lora_on = false;
+  return DLM_OK;
+}
+
+dlm_status dlm_model_enable_lora(dlm_model* m, int32_t on) {
+  g_err[0] = 0;
+  if (!m) return fail(DLM_ERR_INVALID_ARG, "model is NULL");
+  if (on && m->lora_rank == 0) return fail(DLM_ERR_INVALID_ARG, "no adapter set (dlm_model_set_lora)");
+  m->lora_on = on != 0;
+  return DLM_OK;
+}
 
 size_t dlm_workspace_bytes(const dlm_model* m, int32_t max_rows, int32_t max_kv) {
   if (!m || max_rows < 1 || max_kv < 1) return 0;

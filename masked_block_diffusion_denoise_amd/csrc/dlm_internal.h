@@ -26,6 +26,7 @@ struct GemmArgs {
   void* out;            // see epilogue
   int M, N, K;
   int lda, ldc;
+  float alpha = 1.f;    // EPI_RESID_F32: out += alpha * A W^T
   const int* m_dev;     // optional device row count (rows >= *m_dev are skipped); M is the bound
   // EPI_HEAD only
   void* partials;       // MaxSumIdx-like records [n_tiles][M]

@@ -61,10 +61,10 @@ __device__ __forceinline__ void store_quad(const GemmArgs& g, int m, int n, cons
   } else if (EPI == EPI_RESID_F32) {
     float* o = static_cast<float*>(g.out) + static_cast<size_t>(m) * g.ldc + n;
     float4 x = *reinterpret_cast<float4*>(o);
-    x.x += v[0];
-    x.y += v[1];
-    x.z += v[2];
-    x.w += v[3];
+    x.x += g.alpha * v[0];
+    x.y += g.alpha * v[1];
+    x.z += g.alpha * v[2];
+    x.w += g.alpha * v[3];
     *reinterpret_cast<float4*>(o) = x;
   }
 }

@@ -147,6 +147,27 @@ class DlmModel:
     def workspace_bytes(self, max_rows: int, max_kv: int) -> int:
         return int(L.load().dlm_workspace_bytes(self.handle, max_rows, max_kv))
 
+    def set_lora(self, lora: dict | None):
+        """Low-rank adapter on every layer's output projection: {"a": per-layer
+        [rank, H*hd], "b": per-layer [d, rank], "scale": s} (arrays or tensors),
+        or None to remove it.  Left disabled; see enable_lora."""
+        n = self.cfg.n_layers
+        if lora is None:
+            L.call("dlm_model_set_lora", self.handle, None, None, 0, 0.0)
+            self.lora = None
+            return
+        dev = self.device
+        a = [to_bf16_device(x, dev) for x in lora["a"]]
+        b = [to_bf16_device(x, dev) for x in lora["b"]]
+        pa = (C.c_void_p * n)(*[t.data_ptr() for t in a])
+        pb = (C.c_void_p * n)(*[t.data_ptr() for t in b])
+        L.call("dlm_model_set_lora", self.handle, C.cast(pa, C.POINTER(C.c_void_p)),
+               C.cast(pb, C.POINTER(C.c_void_p)), int(a[0].shape[0]), float(lora["scale"]))
+        self.lora = (a, b)  # keeps the device memory alive
+
+    def enable_lora(self, on: bool):
+        L.call("dlm_model_enable_lora", self.handle, int(bool(on)))
+
 
 class KVCache:
     """KV cache in libdlm's layout: k [NL][B][G][cap][hd], v [NL][B][G][cap/16][hd][16] (bf16)."""
@@ -216,13 +237,45 @@ class Session:
         self.max_prefix = 0
 
     # --- the four calls of the ABI, on the current stream ---------------------
-    def prefill(self, tokens: torch.Tensor, ws_rows: int | None = None):
+    def prefill(self, tokens: torch.Tensor, ws_rows: int | None = None, last_argmax: torch.Tensor | None = None,
+                last_conf: torch.Tensor | None = None):
+        """dlm_prefill; with last_argmax (and optionally last_conf) the causal head
+        scores the last prompt position of every row."""
         B, T = tokens.shape
         rows = ws_rows or B * T
         ws, n = self.ws.get(self.m.workspace_bytes(rows, T))
-        L.call("dlm_prefill", self.m.handle, C.byref(self.kv.c), _p(tokens), B, T, _p(self.prefix), None,
-               None, _p(self.flags), ws, n, stream_handle())
+        last_argmax, last_conf = self._head_pair(last_argmax, last_conf, B)
+        L.call("dlm_prefill", self.m.handle, C.byref(self.kv.c), _p(tokens), B, T, _p(self.prefix),
+               _p(last_argmax), _p(last_conf), _p(self.flags), ws, n, stream_handle())
         self.max_prefix = T
+
+    def _head_pair(self, argmax, conf, n):
+        """The entry points take the head's argmax and confidence together."""
+        if (argmax is None) == (conf is None):
+            return argmax, conf
+        if conf is None:
+            conf = torch.empty(argmax.shape, dtype=torch.float32, device=argmax.device)
+        else:
+            argmax = torch.empty(conf.shape, dtype=torch.int32, device=conf.device)
+        assert argmax.numel() == n, (argmax.shape, n)
+        return argmax, conf
+
+    def denoise(self, canvas: torch.Tensor, masked: torch.Tensor, conf: torch.Tensor, argmax: torch.Tensor):
+        """dlm_denoise_step on explicit [B, L] buffers (any L <= 64)."""
+        B, Lb = canvas.shape
+        ws, n = self.ws.get(self.m.workspace_bytes(B * Lb, self.max_prefix + Lb))
+        L.call("dlm_denoise_step", self.m.handle, C.byref(self.kv.c), _p(self.prefix), self.max_prefix,
+               _p(canvas), _p(masked), B, Lb, _p(conf), _p(argmax), None, _p(self.flags), ws, n,
+               stream_handle())
+
+    def append(self, tokens: torch.Tensor, argmax_out=None, conf_out=None):
+        """dlm_append_block of explicit [B, L] tokens (any L <= 64); the prefix grows by L."""
+        B, Lb = tokens.shape
+        ws, n = self.ws.get(self.m.workspace_bytes(B * Lb, self.max_prefix + Lb))
+        argmax_out, conf_out = self._head_pair(argmax_out, conf_out, B * Lb)
+        L.call("dlm_append_block", self.m.handle, C.byref(self.kv.c), _p(self.prefix), self.max_prefix,
+               _p(tokens), B, Lb, _p(argmax_out), _p(conf_out), _p(self.flags), ws, n, stream_handle())
+        self.max_prefix += Lb
 
     def denoise_step(self, logits: torch.Tensor | None = None):
         B, Lb = self.B, self.Lb
@@ -281,3 +334,71 @@ class Session:
             st.steps_per_block.append(steps)
             out.append(self.canvas.clone())
         return torch.cat(out, dim=1), st
+
+    # --- greedy causal decoding -------------------------------------------------
+    def generate_ar(self, prompt: torch.Tensor, n_new: int) -> torch.Tensor:
+        """Greedy causal decoding (one-token appends with the causal head).  [B, n_new]."""
+        B = prompt.shape[0]
+        dev = self.m.device
+        nxt = torch.zeros(B, dtype=torch.int32, device=dev)
+        self.prefill(prompt, last_argmax=nxt)
+        out = [nxt.clone()]
+        arg = torch.zeros(B, 1, dtype=torch.int32, device=dev)
+        for _ in range(n_new - 1):
+            self.append(out[-1].view(B, 1), argmax_out=arg)
+            out.append(arg[:, 0].clone())
+        return torch.stack(out, dim=1)
+
+    # --- linear self-speculation -------------------------------------------------
+    def generate_linear_spec(self, prompt: torch.Tensor, n_new: int, window: int = 32, adaptive: bool = False):
+        """Greedy linear self-speculation for one sequence (MLX guide, sec. 8).
+
+        Each round drafts the canvas [t, MASK x (W - 1)] (t: the known next token)
+        in one bidirectional pass with the model's adapter enabled, then verifies
+        [t, drafts] in one causal pass with it disabled: the longest prefix of
+        drafts equal to the causal argmax is accepted, the causal argmax after it
+        becomes the next known token, and the prefix is trimmed back to the known
+        token plus the accepted drafts.  Adaptive windows start at 8, double (to
+        32) after a fully accepted round and halve after at most half.
+        Returns (tokens [n_new] on the host, accepted drafts per round, windows).
+        """
+        if prompt.shape[0] != 1:
+            raise ValueError("linear self-speculation runs one sequence")
+        dev, mask_id = self.m.device, self.m.cfg.mask_id
+        nxt_t = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.prefill(prompt, last_argmax=nxt_t)
+        nxt = int(nxt_t.item())
+        out, accepted, windows = [], [], []
+        W = 8 if adaptive else window
+        while len(out) < n_new:
+            p0 = self.max_prefix
+            canvas = torch.full((1, W), mask_id, dtype=torch.int32, device=dev)
+            canvas[0, 0] = nxt
+            masked = torch.ones(1, W, dtype=torch.uint8, device=dev)
+            masked[0, 0] = 0
+            conf = torch.zeros(1, W, dtype=torch.float32, device=dev)
+            arg = torch.zeros(1, W, dtype=torch.int32, device=dev)
+            self.m.enable_lora(True)
+            try:
+                self.denoise(canvas, masked, conf, arg)
+            finally:
+                self.m.enable_lora(False)
+            block = arg.clone()
+            block[0, 0] = nxt
+            ver = torch.zeros(1, W, dtype=torch.int32, device=dev)
+            self.append(block, argmax_out=ver)
+            drafts = block[0, 1:].cpu().numpy()
+            verified = ver[0].cpu().numpy()
+            a = 0
+            while a < W - 1 and drafts[a] == verified[a]:
+                a += 1
+            out.extend([nxt] + drafts[:a].tolist())
+            nxt = int(verified[a])
+            self.prefix.fill_(p0 + a + 1)
+            self.max_prefix = p0 + a + 1
+            accepted.append(a)
+            windows.append(W)
+            if adaptive:
+                d = W - 1
+                W = min(2 * W, 32) if a == d else (max(W // 2, 2) if 2 * a <= d else W)
+        return np.array(out[:n_new], dtype=np.int64), accepted, windows

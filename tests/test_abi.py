@@ -171,3 +171,27 @@ def test_status_strings():
     for s in range(-6, 1):
         assert lib.dlm_status_string(s)
     assert lib.dlm_status_string(-6) == b"workspace too small"
+
+
+def test_lora_adapter_validation():
+    lib = L.load()
+    st, h = create(tiny_cfg())
+    assert st == 0
+    try:
+        arr = (C.c_void_p * 2)(4096, 4096)
+        pa = C.cast(arr, C.POINTER(C.c_void_p))
+        bad = (C.c_void_p * 2)(4096, 4100)  # misaligned second layer
+        pb = C.cast(bad, C.POINTER(C.c_void_p))
+        assert lib.dlm_model_enable_lora(h, 1) == -1            # nothing set yet
+        assert lib.dlm_model_set_lora(h, pa, None, 128, 4.0) == -1
+        assert lib.dlm_model_set_lora(h, pa, pa, 64, 4.0) == -4  # rank not a multiple of 128
+        assert lib.dlm_model_set_lora(h, pa, pa, 384, 4.0) == -4  # above DLM_MAX_LORA_RANK
+        assert lib.dlm_model_set_lora(h, pa, pa, 128, float("inf")) == -1
+        assert lib.dlm_model_set_lora(h, pa, pb, 128, 4.0) == -1
+        assert lib.dlm_model_set_lora(h, pa, pa, 128, 4.0) == 0
+        assert lib.dlm_model_enable_lora(h, 1) == 0
+        assert lib.dlm_model_enable_lora(h, 0) == 0
+        assert lib.dlm_model_set_lora(h, None, None, 0, 0.0) == 0  # removal
+        assert lib.dlm_model_enable_lora(h, 1) == -1
+    finally:
+        lib.dlm_model_destroy(h)

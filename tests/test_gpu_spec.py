@@ -1,0 +1,120 @@
+"""Linear self-speculation and greedy AR decoding on the GPU vs the oracle
+(MLX guide, sec. 3.3 and 8): the o_proj adapter in the denoise pass, greedy
+causal decoding with one-token appends, and speculation, which must reproduce
+greedy causal decoding.  Token sequences are compared up to the first position
+whose oracle top-1 logit margin is below 5e-2 (a near tie the bf16 path may
+break the other way)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_helpers import announce, host, i32, rel_rms, sync
+from synth import TINY
+from masked_block_diffusion_denoise_amd import runtime as R
+
+pytestmark = pytest.mark.gpu
+
+GAIN = 30.0          # wide top-1 margins for the token-sequence comparisons
+DENOISE_GAIN = 20.0  # the gain of the other denoise parity tests (confidences well inside (0, 1))
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    w = synth.model_weights(TINY, seed=0, lm_head_gain=GAIN)
+    lora = synth.lora_weights(TINY, rank=128, scale=4.0, seed=1)
+    prompt = synth.prompt(TINY, 1, 12, seed=2)
+    m = R.DlmModel.from_arrays(R.ModelConfig.of(TINY), w)
+    return w, lora, prompt, m
+
+
+def ar_with_margins(w, prompt, n_new):
+    cache, x = oracle.prefill(w, TINY, prompt)
+    toks, margins = [], []
+    for i in range(n_new):
+        lo = oracle.head_logits(w, TINY, x[-1:])[0]
+        top2 = np.sort(lo[np.isfinite(lo)])[-2:]
+        margins.append(top2[1] - top2[0])
+        toks.append(int(np.argmax(lo)))
+        if i + 1 < n_new:
+            x = oracle.forward(w, TINY, np.array([toks[-1]]), cache, mode="causal", write_cache=True)
+    return np.array(toks), np.array(margins)
+
+
+def sure_prefix(margins):
+    bad = np.flatnonzero(margins < 5e-2)
+    return int(bad[0]) if len(bad) else len(margins)
+
+
+@pytest.mark.parametrize("enabled", [True, False])
+def test_denoise_with_adapter(tiny, enabled):
+    announce(f"lora denoise enabled={enabled}")
+    _, lora, prompt, _ = tiny
+    w = synth.model_weights(TINY, seed=0, lm_head_gain=DENOISE_GAIN)
+    m = R.DlmModel.from_arrays(R.ModelConfig.of(TINY), w)
+    m.set_lora(lora)
+    sess = R.Session(m, 1, 128, 16)
+    sess.prefill(i32(prompt))
+    canvas = np.full((1, 16), TINY.mask_id, np.int32)
+    canvas[0, :3] = prompt[0, :3]
+    masked = (canvas == TINY.mask_id).astype(np.uint8)
+    sess.canvas.copy_(i32(canvas))
+    sess.masked.copy_(torch.from_numpy(masked).cuda())
+    logits = torch.zeros(16, TINY.vocab, dtype=torch.float32, device="cuda")
+    m.enable_lora(enabled)
+    try:
+        sess.denoise_step(logits)
+    finally:
+        m.enable_lora(False)
+    sync()
+    cache, _ = oracle.prefill(w, TINY, prompt[0])
+    lo = oracle.denoise_logits(w, TINY, cache, canvas[0], lora=lora if enabled else None)
+    got = host(logits)
+    for j in np.flatnonzero(masked[0]):
+        fin = np.isfinite(lo[j])
+        assert rel_rms(got[j][fin], lo[j][fin]) < 2e-2, j
+    conf_o, _ = oracle.confidence(lo)
+    mk = masked[0] != 0
+    assert np.abs(host(sess.conf)[0][mk] - conf_o[mk]).max() < 1e-2
+    m.set_lora(None)
+
+
+def test_generate_ar_matches_oracle(tiny):
+    announce("greedy AR")
+    w, _, prompt, m = tiny
+    n_new = 24
+    want, margins = ar_with_margins(w, prompt[0], n_new)
+    sess = R.Session(m, 1, 128, 1)
+    got = host(sess.generate_ar(i32(prompt), n_new))[0]
+    k = sure_prefix(margins)
+    assert k >= 4, margins
+    np.testing.assert_array_equal(got[:k], want[:k])
+
+
+@pytest.mark.parametrize("scale,window,adaptive", [(4.0, 8, False), (4.0, 32, False), (0.0, 8, False),
+                                                  (4.0, 8, True)])
+def test_linear_spec_reproduces_greedy_ar(tiny, scale, window, adaptive):
+    announce(f"linear spec scale={scale} window={window} adaptive={adaptive}")
+    w, lora, prompt, m = tiny
+    lo = dict(lora, scale=scale)
+    m.set_lora(lo)
+    n_new = 24
+    want, margins = ar_with_margins(w, prompt[0], n_new)
+    sess = R.Session(m, 1, 128, 32)
+    got, accepted, windows = sess.generate_linear_spec(i32(prompt), n_new, window, adaptive)
+    m.set_lora(None)
+    k = sure_prefix(margins)
+    assert k >= 4, margins
+    np.testing.assert_array_equal(got[:k], want[:k])
+    assert sum(a + 1 for a in accepted) >= n_new
+    assert all(0 <= a < W for a, W in zip(accepted, windows))
+    if adaptive:
+        for (a, W), W2 in zip(zip(accepted, windows), windows[1:]):
+            assert W2 == oracle.next_draft_window(W, a)
+    if scale == 0.0:
+        # without the adapter the draft is the plain denoise pass, which the
+        # oracle shows accepting drafts on this prompt
+        _, acc_o, _, _ = oracle.generate_linear_spec(w, TINY, prompt[0], n_new, lo, window, adaptive)
+        assert sum(acc_o) > 0
+        assert sum(accepted) > 0
