@@ -37,6 +37,9 @@ struct GemmArgs {
   // K-split (set by gemm() when gemm_ksplit() > 1): fp32 [ksplit][M][N] partials
   float* kpart;         // workspace of gemm_workspace_bytes(M, N, K) bytes, from the caller
   int ksplit;
+  // set by gemm() when two launches of different row-tile heights cover one
+  // product: the other launch's height (only the one needing fewer tiles runs)
+  int pick_rows = 0;
 };
 
 int gemm_head_tile_n(int M);                       // vocab columns per EPI_HEAD partial

@@ -137,6 +137,22 @@ __device__ __forceinline__ void lds_frags_2_4(uint32_t a, uint32_t b, u32x4 (&fa
 }
 
 template <int D>
+__device__ __forceinline__ void lds_frags_2_5(uint32_t a, uint32_t b, u32x4 (&fa)[2], u32x4 (&fb)[5]) {
+  asm volatile(
+      "ds_read_b128 %0, %7\n\t"
+      "ds_read_b128 %1, %7 offset:%9\n\t"
+      "ds_read_b128 %2, %8\n\t"
+      "ds_read_b128 %3, %8 offset:%9\n\t"
+      "ds_read_b128 %4, %8 offset:%10\n\t"
+      "ds_read_b128 %5, %8 offset:%11\n\t"
+      "ds_read_b128 %6, %8 offset:%12\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(fa[0]), "=&v"(fa[1]), "=&v"(fb[0]), "=&v"(fb[1]), "=&v"(fb[2]), "=&v"(fb[3]), "=&v"(fb[4])
+      : "v"(a), "v"(b), "i"(D), "i"(2 * D), "i"(3 * D), "i"(4 * D)
+      : "memory");
+}
+
+template <int D>
 __device__ __forceinline__ void lds_frags_2_2(uint32_t a, uint32_t b, u32x4 (&fa)[2], u32x4 (&fb)[2]) {
   asm volatile(
       "ds_read_b128 %0, %4\n\t"
@@ -165,6 +181,8 @@ template <int TN, int TM, int D>
 __device__ __forceinline__ void lds_frags(uint32_t a, uint32_t b, u32x4 (&fa)[TN], u32x4 (&fb)[TM]) {
   if constexpr (TN == 2 && TM == 4)
     lds_frags_2_4<D>(a, b, fa, fb);
+  else if constexpr (TN == 2 && TM == 5)
+    lds_frags_2_5<D>(a, b, fa, fb);
   else if constexpr (TN == 2 && TM == 2)
     lds_frags_2_2<D>(a, b, fa, fb);
   else if constexpr (TN == 1 && TM == 2)
@@ -173,7 +191,13 @@ __device__ __forceinline__ void lds_frags(uint32_t a, uint32_t b, u32x4 (&fa)[TN
     static_assert(TN < 0, "no fragment reader for this wavefront tile");
 }
 
-template <int EPI, int BN, int BM, int WN, int WM, int NBUF, int BK>
+// With DYN the live rows (the device row count) are split evenly, in 32-row
+// units, over the fewest tiles of at most BM rows, so that a count just past a
+// multiple of the tile height does not cost one more pass over the weights;
+// tiles past that number exit.  With g.pick_rows set, two launches with
+// different tile heights cover one product and only the one that needs fewer
+// row tiles for the device row count runs (the shorter one on a tie).
+template <int EPI, int BN, int BM, int WN, int WM, int NBUF, int BK, bool DYN>
 __global__ void __launch_bounds__(WN * WM * 64) k_gemm_tiled(GemmArgs g) {
   constexpr int T = WN * WM * 64;
   constexpr int TN = BN / WN / 32, TM = BM / WM / 32;
@@ -185,14 +209,29 @@ __global__ void __launch_bounds__(WN * WM * 64) k_gemm_tiled(GemmArgs g) {
   static_assert(NBUF >= 2 && NBUF <= 6, "wait ladder covers up to four later stages");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NBUF * STAGE];
 
-  // tile = (weight tile, K range, activation tile), activation tiles fastest
+  // tile = (weight tile, K range, activation tile), activation tiles fastest.
+  // The grid is sized for M rows; the tiles are laid out for the live rows, so
+  // that with a smaller device row count every XCD's live tiles come first in
+  // its dispatch order and the surplus workgroups exit at the end (interleaved
+  // idle workgroups measured ~1.6x slower).
   const int S = EPI == EPI_SPLITK ? g.ksplit : 1;
-  const int nN = g.N / BN, nM = (g.M + BM - 1) / BM;
-  const int total = nN * S * nM, per = (total + 7) / 8;
+  const int live_rows = g.m_dev ? min(g.M, *g.m_dev) : g.M;
+  const int nt = (live_rows + BM - 1) / BM;  // row tiles
+  if (g.pick_rows && (BM > g.pick_rows ? nt >= (live_rows + g.pick_rows - 1) / g.pick_rows
+                                       : nt > (live_rows + g.pick_rows - 1) / g.pick_rows))
+    return;
+  const int total = g.N / BN * S * nt, per = (total + 7) / 8;
+  if (static_cast<int>(blockIdx.x / 8) >= per) return;
   const int tid_ = (blockIdx.x % 8) * per + blockIdx.x / 8;
   if (tid_ >= total) return;
-  const int n0 = (tid_ / (nM * S)) * BN, split = (tid_ / nM) % S, m0 = (tid_ % nM) * BM;
-  const int M = g.m_dev ? min(g.M, *g.m_dev) : g.M;
+  const int n0 = (tid_ / (nt * S)) * BN, split = (tid_ / nt) % S, mi = tid_ % nt;
+  // this tile's rows are [m0, M)
+  int m0 = mi * BM, M = live_rows;
+  if constexpr (DYN) {
+    const int rows = ((live_rows + nt - 1) / nt + 31) & ~31;
+    m0 = mi * rows;
+    M = min(live_rows, m0 + rows);
+  }
   if (m0 >= M) return;
 
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -246,10 +285,11 @@ __global__ void __launch_bounds__(WN * WM * 64) k_gemm_tiled(GemmArgs g) {
     fb_off[s] = BN * ROW + swz<BK>(wm * TM * 32 + arow, 2 * s + ahalf);
   }
   const uint32_t lbase = lds_addr(lds);
-  // A wavefront whose activation rows all lie past the live rows (the ragged
-  // last row tile, e.g. the masked rows of the LM head) still loads its share of
-  // every stage and joins every barrier, but skips its reads and MFMAs.
-  const bool live = m0 + wm * TM * 32 < M;
+  // Activation fragments (32 rows each) past the live rows (the ragged last row
+  // tile, e.g. the masked rows of the LM head) are not multiplied; a wavefront
+  // with none left still loads its share of every stage and joins every
+  // barrier, but skips its reads too.
+  const int live = min(TM, max(0, (M - (m0 + wm * TM * 32) + 31) / 32));
 
 #pragma unroll
   for (int p = 0; p < NBUF - 1; ++p)
@@ -268,7 +308,7 @@ __global__ void __launch_bounds__(WN * WM * 64) k_gemm_tiled(GemmArgs g) {
     else
       wait_vm_barrier<0>();
     if (kt + NBUF - 1 < nk) issue(kt + NBUF - 1);
-    if (!live) continue;
+    if (live == 0) continue;
     const uint32_t sb = lbase + (kt % NBUF) * STAGE;
 #pragma unroll
     for (int s = 0; s < NSTEP; ++s) {
@@ -277,7 +317,8 @@ __global__ void __launch_bounds__(WN * WM * 64) k_gemm_tiled(GemmArgs g) {
 #pragma unroll
       for (int i = 0; i < TN; ++i)
 #pragma unroll
-        for (int j = 0; j < TM; ++j) acc[i][j] = mfma32x32x16(as_bf16x8(fa[i]), as_bf16x8(fb[j]), acc[i][j]);
+        for (int j = 0; j < TM; ++j)
+          if (j < live) acc[i][j] = mfma32x32x16(as_bf16x8(fa[i]), as_bf16x8(fb[j]), acc[i][j]);
     }
   }
 
@@ -432,12 +473,13 @@ size_t gemm_workspace_bytes(int M, int N, int K) {
   return S > 1 ? static_cast<size_t>(S) * M * N * sizeof(float) : 0;
 }
 
-template <int EPI, int BN, int BM, int WN, int WM, int NBUF, int BK = TL_BK>
+template <int EPI, int BN, int BM, int WN, int WM, int NBUF, int BK = TL_BK, bool DYN = false>
 static void launch_tiled(const GemmArgs& g, hipStream_t s) {
   const int S = EPI == EPI_SPLITK ? g.ksplit : 1;
   const int total = (g.N / BN) * S * ((g.M + BM - 1) / BM);
   const int per = (total + 7) / 8;
-  hipLaunchKernelGGL((k_gemm_tiled<EPI, BN, BM, WN, WM, NBUF, BK>), dim3(8 * per), dim3(WN * WM * 64), 0, s, g);
+  hipLaunchKernelGGL((k_gemm_tiled<EPI, BN, BM, WN, WM, NBUF, BK, DYN>), dim3(8 * per), dim3(WN * WM * 64), 0, s,
+                     g);
 }
 
 template <int EPI>
@@ -445,13 +487,24 @@ static hipError_t launch_epi(const GemmArgs& g, hipStream_t s) {
   if constexpr (EPI == EPI_HEAD) {
     // The head streams 1 GB of weights: at up to 128 scored rows it is HBM-bound,
     // and short tiles whose activation rows every wavefront shares from LDS, two
-    // workgroups per CU, keep the most bytes in flight; 256 x 256 tiles otherwise.
-    if (g.M <= 64)
+    // workgroups per CU, keep the most bytes in flight.  Above that, every row
+    // tile is one more pass of the weights through LDS, and the scored-row count
+    // is known only on the device: 256-row tiles and tiles of up to 320 rows
+    // split evenly are both launched, and only the one needing fewer row tiles
+    // runs (e.g. 530 rows: two tiles of 288 rows instead of three).
+    if (g.M <= 64) {
       launch_tiled<EPI, 256, 64, 4, 1, 3>(g, s);
-    else if (g.M <= 128)
+    } else if (g.M <= 128) {
       launch_tiled<EPI, 256, 128, 4, 2, 3>(g, s);
-    else
-      launch_tiled<EPI, 256, 256, 4, 2, 2, 64>(g, s);
+    } else {
+      GemmArgs h = g;
+      h.pick_rows = 320;
+      launch_tiled<EPI, 256, 256, 4, 2, 2, 64>(h, s);
+      if (g.M > 256) {
+        h.pick_rows = 256;
+        launch_tiled<EPI, 256, 320, 4, 2, 2, 64, true>(h, s);
+      }
+    }
   } else if (g.M <= SK_BM) {
     const int S = gemm_ksplit(g.M, g.N, g.K);
     if (S > 1) {

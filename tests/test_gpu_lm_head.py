@@ -57,7 +57,9 @@ def check(R, V, d, mask_id, seed, planted=True, with_logits=True):
 @pytest.mark.parametrize("R,V,d,mask_id", [(16, 4096, 256, 0), (7, 1024, 128, 5), (64, 2048, 512, 2047),
                                            (300, 4096, 256, 100), (40, 1024, 128, 0),
                                            # full 256-row tiles only / 64-row remainder tiles only / both
-                                           (256, 2048, 256, 9), (100, 2048, 256, 3), (577, 1024, 128, 1)])
+                                           (256, 2048, 256, 9), (100, 2048, 256, 3), (577, 1024, 128, 1),
+                                           # rows split evenly over 3 tiles of up to 320 / four 256-row tiles
+                                           (900, 1024, 128, 7), (1000, 1024, 128, 3)])
 def test_lm_head_small(R, V, d, mask_id):
     announce(f"lm head R={R} V={V} d={d}")
     c = check(R, V, d, mask_id, seed=R)
