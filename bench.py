@@ -10,6 +10,13 @@ dlm_denoise_step, one dlm_commit; inputs are resident in HBM before timing.
 
 Prints one JSON line.  Per-kernel times come from HIP events that the library
 records around the kernel inside the real step (dlm_set_kernel_timer).
+
+The same line carries, under "e2e", the full 32-layer 8B-class model (random
+N(0, 0.02) bf16 weights drawn on the device): block-diffusion decoding at batch
+1 (1024-token prompt) and batch 32 (2048-token prompts), a batch-4 run over a
+65536-position synthetic N(0,1) K/V prefix, greedy causal (AR) decoding and
+greedy linear self-speculation with a rank-128 o_proj adapter, 256 generated
+tokens per sequence each (--no-e2e skips them).
 """
 from __future__ import annotations
 
@@ -53,6 +60,13 @@ class HipEvents:
         if self.h.hipEventElapsedTime(C.byref(t), a, b) != 0:
             raise RuntimeError("hipEventElapsedTime failed (event not recorded?)")
         return float(t.value)
+
+    def record(self, e) -> None:
+        """Record e on the stream libdlm launches on (torch's current stream)."""
+        import torch
+        self.h.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
+        if self.h.hipEventRecord(e, C.c_void_p(torch.cuda.current_stream().cuda_stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
 
     def close(self):
         for e in self.events:
@@ -227,12 +241,192 @@ def cpu_baseline(w, shape, B, canvas, masked, P=4096, seed=3, rows=16):
                       f"float64 NumPy), {t:.2f} s per row, scaled to the whole batch"}
 
 
+# ------------------------------------------------------------------ full model
+def _step_bound_ms(shape, B, L, P, masked_rows) -> float:
+    """Roofline of one denoise step of the whole model: per kernel the larger of
+    its HBM and MFMA time, summed over the layers, plus the head."""
+    hw = RL.MI355X_BF16
+    t = 0.0
+    for n in ("qkv", "attention", "o_proj", "gate_up", "down"):
+        by, fl = RL.kernel_work(n, B, L, P, masked_rows, shape.d_model, shape.n_heads, shape.n_kv_heads,
+                                shape.head_dim, shape.d_ffn, shape.vocab)
+        t += shape.n_layers * max(by / hw.hbm_bytes_per_s, fl / hw.flops_per_s)
+    by, fl = RL.kernel_work("lm_head", B, L, P, masked_rows, shape.d_model, shape.n_heads, shape.n_kv_heads,
+                            shape.head_dim, shape.d_ffn, shape.vocab)
+    return 1e3 * (t + max(by / hw.hbm_bytes_per_s, fl / hw.flops_per_s))
+
+
+def e2e_block_diffusion(model, shape, B, T, gen, Lb, max_steps, synthetic_prefix=False, seed=1):
+    """Prefill (or a synthetic N(0,1) K/V prefix), then blocks of denoise + commit
+    until no mask is left (one host read of the rows' remaining masks per step),
+    then the post-block append; threshold 0.9, quota 1."""
+    import torch
+
+    import synth
+    from masked_block_diffusion_denoise_amd import runtime as R
+
+    sess = R.Session(model, B, T + gen + Lb, Lb)
+    dev = model.device
+    prefill_ms = None
+    if synthetic_prefix:
+        c, kv = model.cfg, sess.kv
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed)
+        kv.k.view(c.n_layers, B, c.n_kv_heads, kv.capacity, c.head_dim)[:, :, :, :T].normal_(generator=g)
+        kv.v.view(c.n_layers, B, c.n_kv_heads, kv.capacity // 16, c.head_dim, 16)[:, :, :, :T // 16].normal_(
+            generator=g)
+        sess.prefix.fill_(T)
+        sess.max_prefix = T
+    else:
+        prompt = torch.from_numpy(synth.prompt(shape, B, T, seed=seed)).to(dev)
+        sess.prefill(prompt[:, :min(T, 64)], ws_rows=min(B * T, 8192))  # warm-up of the prefill path
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        sess.prefill(prompt, ws_rows=min(B * T, 8192))
+        torch.cuda.synchronize()
+        prefill_ms = (time.perf_counter() - t0) * 1e3
+    tau = torch.full((B,), 0.9, dtype=torch.float32, device=dev)
+    quota = torch.ones(B, dtype=torch.int32, device=dev)
+    ev = HipEvents()
+    steps, appends, per_block = [], [], []
+    n_blocks = -(-gen // Lb)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n_blocks):
+        sess.begin_block()
+        n = 0
+        while True:
+            a, b = ev.new(), ev.new()
+            ev.record(a)
+            sess.denoise_step()
+            sess.commit(tau, quota, max_steps)
+            ev.record(b)
+            steps.append((a, b))
+            n += 1
+            if int(sess.n_left.max().item()) == 0:
+                break
+        a, b = ev.new(), ev.new()
+        ev.record(a)
+        sess.append_block()
+        ev.record(b)
+        appends.append((a, b))
+        per_block.append(n)
+    torch.cuda.synchronize()
+    decode_s = time.perf_counter() - t0
+    step_ms = sum(ev.ms(a, b) for a, b in steps) / len(steps)
+    append_ms = sum(ev.ms(a, b) for a, b in appends) / len(appends)
+    ev.close()
+    tokens = B * n_blocks * Lb
+    nfe = len(steps)
+    # masked rows scored, averaged over the steps: each step of a block commits
+    # one position per row until the last allowed step commits the rest
+    masked = sum(B * (Lb - s) for blk in per_block for s in range(blk)) / nfe
+    bound = _step_bound_ms(shape, B, Lb, T + gen // 2, masked)
+    del sess
+    torch.cuda.empty_cache()
+    out = {"batch": B, "prompt": T, "synthetic_prefix": synthetic_prefix, "generated_per_row": n_blocks * Lb,
+           "block": Lb, "max_steps": max_steps,
+           "decode_s": round(decode_s, 4), "committed_tokens_per_s": round(tokens / decode_s, 2),
+           "denoise_nfe": nfe, "post_block_nfe": n_blocks, "tokens_per_forward": round(n_blocks * Lb / nfe, 3),
+           "ms_per_denoise_step": round(step_ms, 4), "denoise_steps_per_s": round(1e3 / step_ms, 3),
+           "ms_per_append": round(append_ms, 4), "steps_per_block": per_block,
+           "step_roofline_ms": round(bound, 4), "step_roofline_frac": round(bound / step_ms, 4)}
+    if prefill_ms is not None:
+        out["prefill_ms"] = round(prefill_ms, 3)
+        out["e2e_tokens_per_s"] = round(tokens / (decode_s + prefill_ms / 1e3), 2)
+    return out
+
+
+def e2e_ar(model, shape, T, n_new, seed=1):
+    """Greedy causal decoding at batch 1: prefill, then one-token appends."""
+    import torch
+
+    import synth
+    from masked_block_diffusion_denoise_amd import runtime as R
+
+    sess = R.Session(model, 1, T + n_new + 64, 1)
+    prompt = torch.from_numpy(synth.prompt(shape, 1, T, seed=seed)).to(model.device)
+    sess.generate_ar(prompt[:, :64], 4)  # warm-up
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    toks = sess.generate_ar(prompt, n_new)
+    torch.cuda.synchronize()
+    total = time.perf_counter() - t0
+    del sess
+    torch.cuda.empty_cache()
+    return {"batch": 1, "prompt": T, "generated": n_new, "e2e_s": round(total, 4),
+            "e2e_tokens_per_s": round(n_new / total, 2)}, toks.cpu().numpy()[0]
+
+
+def e2e_linear_spec(model, shape, T, n_new, window=32, rank=128, scale=4.0, seed=1, ar_tokens=None):
+    """Greedy linear self-speculation at batch 1 with a random-init rank-128
+    adapter (N(0, 0.02)) on every layer's output projection, used by the draft."""
+    import numpy as np
+    import torch
+
+    import synth
+    from masked_block_diffusion_denoise_amd import runtime as R
+
+    c, dev = model.cfg, model.device
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed + 100)
+    rn = lambda *s: torch.empty(*s, dtype=torch.bfloat16, device=dev).normal_(0.0, 0.02, generator=g)
+    model.set_lora({"a": [rn(rank, c.n_heads * c.head_dim) for _ in range(c.n_layers)],
+                    "b": [rn(c.d_model, rank) for _ in range(c.n_layers)], "scale": scale})
+    sess = R.Session(model, 1, T + n_new + 2 * window, window)
+    prompt = torch.from_numpy(synth.prompt(shape, 1, T, seed=seed)).to(dev)
+    sess.generate_linear_spec(prompt[:, :64], 4, window)  # warm-up
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    toks, accepted, _ = sess.generate_linear_spec(prompt, n_new, window)
+    torch.cuda.synchronize()
+    total = time.perf_counter() - t0
+    model.set_lora(None)
+    del sess
+    torch.cuda.empty_cache()
+    out = {"batch": 1, "prompt": T, "generated": n_new, "window": window, "lora_rank": rank, "lora_scale": scale,
+           "rounds": len(accepted), "mean_accepted_drafts": round(float(np.mean(accepted)), 3),
+           "tokens_per_round": round(n_new / len(accepted), 3), "accepted_per_round": accepted,
+           "e2e_s": round(total, 4), "e2e_tokens_per_s": round(n_new / total, 2)}
+    if ar_tokens is not None:
+        same = np.asarray(toks[:n_new]) == np.asarray(ar_tokens[:n_new])
+        out["agrees_with_ar_for_first"] = int(n_new if same.all() else np.argmin(same))
+    return out
+
+
+def run_e2e(gen=256) -> dict:
+    import torch
+
+    import synth
+    from masked_block_diffusion_denoise_amd import runtime as R
+
+    shape = synth.DENSE_8B
+    print("[bench] e2e: drawing 8B-class weights on the device", file=sys.stderr, flush=True)
+    model = R.DlmModel.random(R.ModelConfig.of(shape), seed=0)
+    res = {"model": "dense 8B-class, 32 layers, d 4096, 32/8 heads x 128, SwiGLU 14336, vocab 131072, "
+                    "random N(0,0.02) bf16 weights"}
+    legs = [("block_diffusion_b1", dict(B=1, T=1024, gen=gen, Lb=32, max_steps=32)),
+            ("block_diffusion_b32", dict(B=32, T=2048, gen=gen, Lb=32, max_steps=16)),
+            ("long_prefix_b4", dict(B=4, T=65536, gen=gen, Lb=32, max_steps=16, synthetic_prefix=True))]
+    for name, kw in legs:
+        print(f"[bench] e2e {name}", file=sys.stderr, flush=True)
+        res[name] = e2e_block_diffusion(model, shape, **kw)
+    print("[bench] e2e ar_b1", file=sys.stderr, flush=True)
+    res["ar_b1"], ar_tokens = e2e_ar(model, shape, 1024, gen)
+    print("[bench] e2e linear_spec_b1", file=sys.stderr, flush=True)
+    res["linear_spec_b1"] = e2e_linear_spec(model, shape, 1024, gen, ar_tokens=ar_tokens)
+    del model
+    torch.cuda.empty_cache()
+    return res
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-e2e", action="store_true", help="skip the full 32-layer model runs")
     ap.add_argument("--batches", default="32,1", help="batch sizes; the first is the headline")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run a plain copy of this many MiB first (scale for counter runs)")
@@ -302,6 +496,10 @@ def main(argv=None) -> int:
         out[f"b{B}"] = {"steps_per_s": round(r["steps_per_s"], 3), "ms_per_step": round(r["ms_per_step"], 4),
                         "committed_tokens_per_s": round(r["committed_tokens_per_s"], 2),
                         "kernels": {n: {"ms": k["ms"], **k["roofline"]} for n, k in r["kernels"].items()}}
+    del model, res
+    torch.cuda.empty_cache()
+    if not a.no_e2e:
+        out["e2e"] = run_e2e()
     if not a.no_cpu:
         print(f"[bench] cpu oracle baseline", file=sys.stderr, flush=True)
         canvas, masked = head["inputs"]
