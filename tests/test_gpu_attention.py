@@ -74,6 +74,12 @@ def test_attention_batch32_prefix4096():
     run_case(32, 32, 32, 8, 128, [4096] * 32, 0, 0, seed=7, check_rows=[0, 17, 31])
 
 
+def test_attention_batch4_prefix65536():
+    announce("attention b4 p65536")
+    # the long-context decode shape: 64-way split KV, every row ragged by 3
+    run_case(4, 32, 32, 8, 128, [65536, 65533, 65530, 65527], 0, 0, seed=10, check_rows=[0, 3])
+
+
 @pytest.mark.parametrize("hd,H,G", [(32, 4, 2), (128, 32, 8)])
 @pytest.mark.parametrize("causal", [0, 1])
 def test_attention_ignores_slots_past_the_end(hd, H, G, causal):

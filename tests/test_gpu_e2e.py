@@ -1,0 +1,154 @@
+"""The full 32-layer 8B-class model on the GPU, with random-init bf16 weights
+(N(0, 0.02)) drawn on the device.  No oracle runs at this size; the tests check
+what holds at any size:
+
+* the commit rule (BlockRefinement in the "Diffusion LLMs" module, sec. 9): with
+  no confidence above the 0.9 threshold (random init), exactly the quota (one
+  position, the most confident, lowest index on ties) is committed per step and
+  the last allowed step commits every remaining mask; committed positions never
+  change;
+* the post-block causal pass writes the same keys and values as a causal
+  prefill of prompt + block (Module 12, sec. 14), to within the spread between
+  two chunkings of that prefill;
+* linear self-speculation (MLX guide, sec. 8) accounting: whole rounds of at
+  most W - 1 accepted drafts plus one correction, and a cache trimmed to the
+  kept tokens.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_helpers import announce, host, i32, rel_rms, sync
+from masked_block_diffusion_denoise_amd import runtime as R
+
+pytestmark = pytest.mark.gpu
+
+SHAPE = synth.DENSE_8B
+MASK = SHAPE.mask_id
+
+
+@pytest.fixture(scope="module")
+def dense8b():
+    announce("drawing 8B-class weights on the device")
+    m = R.DlmModel.random(R.ModelConfig.of(SHAPE), seed=0)
+    yield m
+    del m
+    torch.cuda.empty_cache()
+
+
+def denoise_block_checked(sess, max_steps, check_rows):
+    """One block of denoise + commit (threshold 0.9, quota 1); every step checks
+    the commit of `check_rows` against the rule applied on the host to the
+    same confidences, and the counts of every row.  Returns the step count."""
+    B, L = sess.B, sess.Lb
+    tau = torch.full((B,), 0.9, dtype=torch.float32, device="cuda")
+    quota = torch.ones(B, dtype=torch.int32, device="cuda")
+    sess.begin_block()
+    for step in range(max_steps):
+        sess.denoise_step()
+        sync()
+        canvas0, masked0 = host(sess.canvas), host(sess.masked).astype(bool)
+        conf, arg = host(sess.conf), host(sess.argmax)
+        sess.commit(tau, quota, max_steps)
+        sync()
+        canvas1, masked1 = host(sess.canvas), host(sess.masked).astype(bool)
+        n_com, n_left = host(sess.n_committed), host(sess.n_left)
+        left0 = masked0.sum(1)
+        last = step == max_steps - 1
+        want_n = np.where(last, left0, np.minimum(1, left0))
+        np.testing.assert_array_equal(n_com, want_n)
+        np.testing.assert_array_equal(n_left, left0 - want_n)
+        np.testing.assert_array_equal(masked1.sum(1), left0 - want_n)
+        assert not (masked1 & ~masked0).any()                       # never remasked
+        np.testing.assert_array_equal(canvas1[~masked0], canvas0[~masked0])  # committed stay
+        assert (canvas1[masked1] == MASK).all() and (canvas1[~masked1] != MASK).all()
+        for b in check_rows:
+            js = np.flatnonzero(masked0[b])
+            assert np.isfinite(conf[b, js]).all() and (conf[b, js] > 0).all()
+            assert conf[b, js].max() < 0.9, "random init: no confidence reaches the threshold"
+            assert (arg[b, js] != MASK).all()
+            order = sorted(js, key=lambda j: (-conf[b, j], j))
+            chosen = sorted(order[:want_n[b]])
+            np.testing.assert_array_equal(np.flatnonzero(masked0[b] & ~masked1[b]), chosen)
+            np.testing.assert_array_equal(canvas1[b, chosen], arg[b, chosen])
+        if n_left.max() == 0:
+            return step + 1
+    return max_steps
+
+
+def test_dense8b_block_batch1_commit_rule_and_append(dense8b):
+    announce("8B model: one block at batch 1, then append vs prefill")
+    T, L = 1024, 32
+    prompt = synth.prompt(SHAPE, 1, T, seed=1)
+    sess = R.Session(dense8b, 1, T + 64, L)
+    sess.prefill(i32(prompt))
+    steps = denoise_block_checked(sess, 32, check_rows=[0])
+    assert steps == 32
+    block = host(sess.canvas)
+    sess.append_block()
+    sync()
+    assert int(host(sess.prefix)[0]) == T + L
+
+    # The same sequence prefilled in one pass, and in 256-position passes: the
+    # two differ only in summation order and bf16 rounding, and that spread
+    # (growing with depth at random init) is the bar for the appended block.
+    def prefill(ws_rows=None):
+        r = R.Session(dense8b, 1, T + 64, L)
+        r.prefill(i32(np.concatenate([prompt, block], axis=1)), ws_rows=ws_rows)
+        sync()
+        return r
+
+    one, chunked = prefill(), prefill(ws_rows=256)
+    for kind in ("k_logical", "v_logical"):
+        got, want, alt = (getattr(x.kv, kind)() for x in (sess, one, chunked))
+        for layer in range(SHAPE.n_layers):
+            g, w, a = (host(t[layer, 0, :, T:T + L]).ravel() for t in (got, want, alt))
+            spread = rel_rms(a, w)
+            err = rel_rms(g, w)
+            assert err <= 1.25 * spread + 1e-3, (kind, layer, err, spread)
+            if layer < 2:
+                assert err < 2e-2, (kind, layer, err)
+    del sess, one, chunked
+    torch.cuda.empty_cache()
+
+
+def test_dense8b_block_batch32_forced_completion(dense8b):
+    announce("8B model: one block at batch 32, 2048-token prompts, 16 steps")
+    T, L = 2048, 32
+    prompt = synth.prompt(SHAPE, 32, T, seed=2)
+    sess = R.Session(dense8b, 32, T + 64, L)
+    sess.prefill(i32(prompt), ws_rows=8192)
+    steps = denoise_block_checked(sess, 16, check_rows=[0, 13, 31])
+    assert steps == 16
+    sess.append_block()
+    sync()
+    assert (host(sess.prefix) == T + L).all()
+    del sess
+    torch.cuda.empty_cache()
+
+
+def test_dense8b_linear_spec_accounting(dense8b):
+    announce("8B model: linear self-speculation accounting")
+    T, n_new, W = 1024, 48, 32
+    c = dense8b.cfg
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    rn = lambda *s: torch.empty(*s, dtype=torch.bfloat16, device="cuda").normal_(0.0, 0.02, generator=g)
+    dense8b.set_lora({"a": [rn(128, c.n_heads * c.head_dim) for _ in range(c.n_layers)],
+                      "b": [rn(c.d_model, 128) for _ in range(c.n_layers)], "scale": 4.0})
+    prompt = i32(synth.prompt(SHAPE, 1, T, seed=3))
+    try:
+        sess = R.Session(dense8b, 1, T + n_new + 2 * W, W)
+        toks, accepted, windows = sess.generate_linear_spec(prompt, n_new, W)
+    finally:
+        dense8b.set_lora(None)
+    sync()
+    assert len(toks) == n_new and (toks != MASK).all()
+    assert all(0 <= a < w for a, w in zip(accepted, windows)) and set(windows) == {W}
+    kept = sum(a + 1 for a in accepted)
+    assert kept >= n_new and kept - (accepted[-1] + 1) < n_new
+    assert sess.max_prefix == T + kept and int(host(sess.prefix)[0]) == T + kept
+    ar = host(R.Session(dense8b, 1, T + n_new + 64, 1).generate_ar(prompt, n_new))[0]
+    assert toks[0] == ar[0]  # both take the prefill's causal argmax
+    torch.cuda.empty_cache()
