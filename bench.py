@@ -99,8 +99,11 @@ TIMERS = {"lm_head": 0, "attention": 1, "gate_up": 2, "down": 3, "qkv": 4}
 
 # LM-head launches in a counter run, told apart from the other GEMMs by the
 # head epilogue's template argument and the tile (k_gemm_tiled<EPI, BN, BM, ...>,
-# EPI_HEAD = 3): 256 x 256 tiles at batch 32, 256 x 64 tiles at batch 1.
-HEAD_KERNELS = {"lm_head_b32": re.compile(r"k_gemm_tiled<3, 256, 256,"), "lm_head_b1": re.compile(r"k_gemm_tiled<3, 256, 64,")}
+# EPI_HEAD = 3).  At batch 32 one head is two launches, 256-row and up-to-320-row
+# tiles, of which only one does the work (the other reads the row count and
+# exits); a head's bytes are the sum of the two.  Batch 1: 256 x 64 tiles.
+HEAD_KERNELS = {"lm_head_b32": [re.compile(r"k_gemm_tiled<3, 256, 256,"), re.compile(r"k_gemm_tiled<3, 256, 320,")],
+                "lm_head_b1": [re.compile(r"k_gemm_tiled<3, 256, 64,")]}
 COPY_KERNEL = re.compile(r"copyBuffer")
 
 
@@ -142,11 +145,14 @@ def traffic_from(fetch_dir: str, write_dir: str, copy_mib: int, command: str) ->
             raise SystemExit(f"no copy dispatch with {counter} in {d}")
         scale = (copy_mib << 20) / (max(copies) * 1024.0)
         out[f"{counter.lower()}_scale"] = round(scale, 4)
-        for key, pat in HEAD_KERNELS.items():
-            launches = [x for k, v in vals.items() if pat.search(k) for x in v]
-            if not launches:
+        for key, pats in HEAD_KERNELS.items():
+            kib = 0.0
+            for pat in pats:
+                launches = [x for k, v in vals.items() if pat.search(k) for x in v]
+                if launches:
+                    kib += sum(launches) / len(launches)
+            if kib == 0.0:
                 continue
-            kib = sum(launches) / len(launches)
             out["raw_kib"][f"{key}_{counter}"] = round(kib, 1)
             out["per_launch_bytes"][key] = out["per_launch_bytes"].get(key, 0) + round(kib * 1024.0 * scale)
     return out
