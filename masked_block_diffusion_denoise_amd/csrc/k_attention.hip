@@ -34,13 +34,11 @@ namespace dlm {
 
 constexpr int KT = 32;          // keys per tile
 constexpr int MIN_CHUNK = 256;  // minimum keys per split (8 tiles)
-// Launch shapes.  Wide batches (many (row, group) pairs): about 512 workgroups,
-// two per CU, each with a 3-stage ring -- the other workgroup on the CU hides
-// latency.  Narrow batches (batch 1-4): about 256 workgroups with a 6-stage ring,
-// each workgroup alone on its CU with five tiles in flight.
-constexpr int WIDE_BASE = 128;   // (row, group, query block) count from which a batch is wide
-constexpr int WIDE_TARGET = 512, WIDE_NBUF = 3;
-constexpr int NARROW_TARGET = 256, NARROW_NBUF = 6;
+// Launch shape: about 512 workgroups (two per CU), each with a 3-stage ring, so
+// that the other workgroup on a CU hides the latency of a tile's dependent chain
+// (one workgroup per CU with a deeper ring measured up to 25% slower at batch 4
+// over a 65536-position prefix, and no faster at batch 1).
+constexpr int TARGET_WG = 512, ATT_STAGES = 3;
 constexpr float RESCALE = 8.f;  // lazy-rescale threshold (log2 units)
 
 __device__ __forceinline__ uint32_t att_lds_addr(const void* p) {
@@ -390,8 +388,7 @@ __global__ void __launch_bounds__(256) k_attn_merge(AttnArgs a, int splits) {
 int attn_splits(const AttnArgs& a, int* chunk_out) {
   const int qblocks = (a.Lq + 31) / 32;
   const long base = static_cast<long>(qblocks) * a.B * a.G;
-  const long target = base >= WIDE_BASE ? WIDE_TARGET : NARROW_TARGET;
-  int splits = static_cast<int>((target + base - 1) / base);
+  int splits = static_cast<int>((TARGET_WG + base - 1) / base);
   const int max_splits = std::max(1, a.max_kv / MIN_CHUNK);
   splits = std::max(1, std::min({splits, max_splits, 64}));
   int chunk = (a.max_kv + splits - 1) / splits;
@@ -408,8 +405,7 @@ size_t attn_partial_floats(int splits, int rows, int H, int hd) {
 
 size_t attn_partial_floats_bound(int R, int H, int G, int hd, int max_kv) {
   // splits <= min(ceil(max target / G), max_kv / MIN_CHUNK, 64) for any B, Lq with B*Lq <= R
-  const int target = std::max(WIDE_TARGET, NARROW_TARGET);
-  const int s = std::max(1, std::min({(target + G - 1) / G, max_kv / MIN_CHUNK, 64}));
+  const int s = std::max(1, std::min({(TARGET_WG + G - 1) / G, max_kv / MIN_CHUNK, 64}));
   return attn_partial_floats(s, R, H, hd);
 }
 
@@ -419,10 +415,7 @@ static hipError_t launch(const AttnArgs& a, hipStream_t s) {
   const int splits = attn_splits(a, &chunk);
   const int qblocks = (a.Lq + 31) / 32;
   dim3 grid(splits, qblocks, a.B * a.G);
-  if (static_cast<long>(qblocks) * a.B * a.G >= WIDE_BASE)
-    hipLaunchKernelGGL((k_attn<HD, GS, WIDE_NBUF>), grid, dim3(GS * 64), 0, s, a, chunk);
-  else
-    hipLaunchKernelGGL((k_attn<HD, GS, NARROW_NBUF>), grid, dim3(GS * 64), 0, s, a, chunk);
+  hipLaunchKernelGGL((k_attn<HD, GS, ATT_STAGES>), grid, dim3(GS * 64), 0, s, a, chunk);
   if (splits > 1) {
     const int pairs = a.B * a.Lq * a.H;
     hipLaunchKernelGGL((k_attn_merge<HD>), dim3((pairs + 3) / 4), dim3(256), 0, s, a, splits);
