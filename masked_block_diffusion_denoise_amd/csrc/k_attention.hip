@@ -20,11 +20,15 @@
 // index fastest ([cap/16][hd][16]).  So the V operand is one 16-byte LDS read per
 // MFMA and no transpose is needed anywhere.
 //
-// K/V tiles stream through a ring of NBUF LDS stages filled by direct
-// global-to-LDS loads (global_load_lds_dwordx4), NBUF - 1 tiles in flight, one
-// wait + barrier per tile; fragments are read in inline asm that waits for its
-// own reads (the compiler cannot tell the ring stages apart and would otherwise
-// drain every load before each read).
+// K/V tiles stream through a ring of two LDS stages of two tiles each, filled
+// by direct global-to-LDS loads (global_load_lds_dwordx4): one stage is in
+// flight while the other is used, one wait + barrier per stage.  The two tiles
+// of a stage are computed together (one softmax update over 64 keys), which
+// gives each wavefront independent MFMA chains to overlap -- with one or two
+// wavefronts per SIMD, a single tile's dependent chain (S product, softmax,
+// P*V) left the matrix unit idle most of the time.  Fragments are read in
+// inline asm that waits for its own reads (the compiler cannot tell the ring
+// stages apart and would otherwise drain every load before each read).
 #include <algorithm>
 
 #include "dlm_device.h"
@@ -38,7 +42,8 @@ constexpr int MIN_CHUNK = 256;  // minimum keys per split (8 tiles)
 // that the other workgroup on a CU hides the latency of a tile's dependent chain
 // (one workgroup per CU with a deeper ring measured up to 25% slower at batch 4
 // over a 65536-position prefix, and no faster at batch 1).
-constexpr int TARGET_WG = 512, ATT_STAGES = 3;
+constexpr int TARGET_WG = 512;
+constexpr int SUB = 2;  // 32-key tiles per ring stage (two stages in the ring)
 constexpr float RESCALE = 8.f;  // lazy-rescale threshold (log2 units)
 
 __device__ __forceinline__ uint32_t att_lds_addr(const void* p) {
@@ -107,17 +112,17 @@ __device__ __forceinline__ void lds_read_n<2>(const uint32_t (&a)[2], u32x4 (&f)
                : "memory");
 }
 
-template <int HD, int GS, int ATT_NBUF>
+template <int HD, int GS>
 __global__ void __launch_bounds__(GS * 64) k_attn(AttnArgs a, int chunk_len) {
   constexpr int KCH = HD / 8;              // 16-byte chunks per key row
   constexpr int TILE_K = KT * HD * 2;      // bytes of a K tile (= bytes of a V tile)
-  constexpr int STAGE = 2 * TILE_K;
-  constexpr int NBLK = STAGE / 1024;       // 1 KB load blocks per stage
-  constexpr int BLK = NBLK / GS;           // ... per wavefront
-  static_assert(NBLK % GS == 0 && BLK >= 1, "stage must split evenly over the wavefronts");
+  constexpr int TILE = 2 * TILE_K;         // one 32-key tile: K, then V
+  constexpr int STAGE = SUB * TILE;        // one ring stage: SUB tiles
+  constexpr int TBLK = TILE / 1024 / GS;   // 1 KB load blocks per wavefront per tile
+  static_assert((TILE / 1024) % GS == 0 && TBLK >= 1, "a tile must split evenly over the wavefronts");
   constexpr int NS = HD / 16;              // 16-deep steps of the S product
   constexpr int ND = HD / 32;              // 32-row blocks of the output
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[ATT_NBUF * STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE];
 
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int split = blockIdx.x, qb = blockIdx.y;
@@ -132,6 +137,7 @@ __global__ void __launch_bounds__(GS * 64) k_attn(AttnArgs a, int chunk_len) {
   int kend = min(kv_len, kbeg + chunk_len);
   if (a.causal) kend = min(kend, p0 + min(qb * 32 + 32, a.Lq));
   const int ntiles = kend > kbeg ? (kend - kbeg + KT - 1) / KT : 0;
+  const int nst = (ntiles + SUB - 1) / SUB;  // ring stages
 
   const int splits = gridDim.x;
   const size_t mrow = static_cast<size_t>(b) * a.Lq + jq;  // output row
@@ -157,33 +163,40 @@ __global__ void __launch_bounds__(GS * 64) k_attn(AttnArgs a, int chunk_len) {
   const bf16_t* kc = static_cast<const bf16_t*>(a.kc) + head_off;
   const bf16_t* vc = static_cast<const bf16_t*>(a.vc) + head_off;
 
-  // Load block q of a stage, lane l -> 16-byte slot 64q + l of the stage.  K
-  // blocks (q < NBLK/2): slot -> (row, physical chunk) -> logical chunk of key
-  // k0 + row.  V blocks: the V tile is contiguous in the blocked cache layout
-  // ([2][HD][16] keys from k0), slot -> (vrow, physical half) -> logical half.
-  // Both tile bases sit at element k0*HD of their cache.
-  const bf16_t* src[BLK];
+  // Load block q of a tile, lane l -> 16-byte slot 64q + l of the tile.  K
+  // blocks (q < TILE/2048): slot -> (row, physical chunk) -> logical chunk of
+  // key k0 + row.  V blocks: the V tile is contiguous in the blocked cache
+  // layout ([2][HD][16] keys from k0), slot -> (vrow, physical half) -> logical
+  // half.  Both tile bases sit at element k0*HD of their cache.
+  const bf16_t* src[TBLK];
 #pragma unroll
-  for (int i = 0; i < BLK; ++i) {
-    const int q = w * BLK + i;
-    if (q < NBLK / 2) {
+  for (int i = 0; i < TBLK; ++i) {
+    const int q = w * TBLK + i;
+    if (q < TILE / 2048) {
       const int slot = q * 64 + lane;
       const int row = slot / KCH, pc = slot % KCH;
       src[i] = kc + row * HD + (pc ^ kxor<HD>(row)) * 8;
     } else {
-      const int slot = (q - NBLK / 2) * 64 + lane;
+      const int slot = (q - TILE / 2048) * 64 + lane;
       const int vrow = slot >> 1, ph = slot & 1;
       src[i] = vc + vrow * 16 + (ph ^ vxor(vrow)) * 8;
     }
   }
-  auto issue = [&](int t) {  // tile t of this workgroup's key range
-    uint8_t* dst = lds + (t % ATT_NBUF) * STAGE + w * BLK * 1024;
-    const size_t off = static_cast<size_t>(kbeg + t * KT) * HD;
+  // stage st: tiles st*SUB .. st*SUB+SUB-1 of this workgroup's key range; a tile
+  // past the range is not loaded (its keys are masked and its values zeroed)
+  auto issue = [&](int st) {
 #pragma unroll
-    for (int i = 0; i < BLK; ++i) att_load_lds16(src[i] + off, dst + i * 1024);
+    for (int u = 0; u < SUB; ++u) {
+      const int t = st * SUB + u;
+      if (t >= ntiles) break;
+      uint8_t* dst = lds + (st & 1) * STAGE + u * TILE + w * TBLK * 1024;
+      const size_t off = static_cast<size_t>(kbeg + t * KT) * HD;
+#pragma unroll
+      for (int i = 0; i < TBLK; ++i) att_load_lds16(src[i] + off, dst + i * 1024);
+    }
   };
 
-  // fragment offsets within a stage
+  // fragment offsets within a tile
   const int ar = lane & 31;
   const int krow = (ar & ~12) | ((ar & 4) << 1) | ((ar & 8) >> 1);  // bits 2 and 3 swapped
   uint32_t koff[NS];
@@ -193,68 +206,67 @@ __global__ void __launch_bounds__(GS * 64) k_attn(AttnArgs a, int chunk_len) {
   const uint32_t voff = TILE_K + ar * 32 + ((half ^ vxor(ar)) << 4);
   const uint32_t lbase = att_lds_addr(lds);
 
-#pragma unroll
-  for (int p = 0; p < ATT_NBUF - 1; ++p)
-    if (p < ntiles) issue(p);
-  for (int t = 0; t < ntiles; ++t) {
-    // vmcnt counts at most 63: waiting for fewer outstanding loads is only stricter
-    const int later = min(ntiles - 1 - t, ATT_NBUF - 2);
-    if (later >= 4)
-      att_wait_barrier<std::min(4 * BLK, 63)>();
-    else if (later == 3)
-      att_wait_barrier<std::min(3 * BLK, 63)>();
-    else if (later == 2)
-      att_wait_barrier<2 * BLK>();
-    else if (later == 1)
-      att_wait_barrier<BLK>();
-    else
-      att_wait_barrier<0>();
-    if (t + ATT_NBUF - 1 < ntiles) issue(t + ATT_NBUF - 1);
-    const int k0 = kbeg + t * KT;
-    const uint32_t sb = lbase + (t % ATT_NBUF) * STAGE;
+  if (nst > 0) issue(0);
+  for (int st = 0; st < nst; ++st) {
+    // two stages: stage st has landed once no load is outstanding; the barrier
+    // also retires stage st - 1, which the next issue refills
+    att_wait_barrier<0>();
+    if (st + 1 < nst) issue(st + 1);
+    const int k0 = kbeg + st * SUB * KT;
+    const uint32_t sb = lbase + (st & 1) * STAGE;
 
-    // two independent accumulation chains (even / odd steps) halve the MFMA
-    // dependency chain of the S product
-    f32x16 sacc, sodd;
+    // S of the SUB tiles: two independent accumulation chains per tile (even /
+    // odd steps); fragment reads in batches of KB steps per tile (register
+    // pressure), KB even so that each batch feeds both chains
+    f32x16 sacc[SUB], sodd[SUB];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sacc[r] = sodd[r] = 0.f;
-    // fragment reads in batches of KB (two batches at hd 128: register pressure);
-    // KB is even so that each batch feeds both chains
+    for (int u = 0; u < SUB; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[u][r] = sodd[u][r] = 0.f;
     constexpr int KB = NS >= 8 ? NS / 2 : NS;
     static_assert(KB % 2 == 0 && NS % KB == 0, "batches of an even number of K fragments");
 #pragma unroll
     for (int hs = 0; hs < NS; hs += KB) {
-      uint32_t ka[KB];
-      u32x4 kf[KB];
+      uint32_t ka[SUB * KB];
+      u32x4 kf[SUB * KB];
 #pragma unroll
-      for (int s = 0; s < KB; ++s) ka[s] = sb + koff[hs + s];
-      lds_read_n<KB>(ka, kf);
+      for (int u = 0; u < SUB; ++u)
 #pragma unroll
-      for (int s = 0; s < KB; s += 2) {
-        sacc = mfma32x32x16(as_bf16x8(kf[s]), qf[hs + s], sacc);
-        sodd = mfma32x32x16(as_bf16x8(kf[s + 1]), qf[hs + s + 1], sodd);
-      }
+        for (int s = 0; s < KB; ++s) ka[u * KB + s] = sb + u * TILE + koff[hs + s];
+      lds_read_n<SUB * KB>(ka, kf);
+#pragma unroll
+      for (int s = 0; s < KB; s += 2)
+#pragma unroll
+        for (int u = 0; u < SUB; ++u) {
+          sacc[u] = mfma32x32x16(as_bf16x8(kf[u * KB + s]), qf[hs + s], sacc[u]);
+          sodd[u] = mfma32x32x16(as_bf16x8(kf[u * KB + s + 1]), qf[hs + s + 1], sodd[u]);
+        }
     }
+    // register r of tile u holds key k0 + u*KT + 16*(r/8) + 8*half + (r%8).
+    // Only the last tiles of the range and causal passes need a mask.
+    bool tail[SUB];
+    float mloc = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sacc[r] += sodd[r];
-    // register r holds key k0 + 16*(r/8) + 8*half + (r%8).  Only the last tile
-    // of the range and causal passes need a mask.
-    const bool tail = k0 + KT > kend;
-    if (tail || a.causal) {
+    for (int u = 0; u < SUB; ++u) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = k0 + 16 * (r >> 3) + 8 * half + (r & 7);
-        if (key >= kend || (a.causal && key > qpos)) sacc[r] = -INFINITY;
+      for (int r = 0; r < 16; ++r) sacc[u][r] += sodd[u][r];
+      const int ku = k0 + u * KT;
+      tail[u] = ku + KT > kend;
+      if (tail[u] || a.causal) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = ku + 16 * (r >> 3) + 8 * half + (r & 7);
+          if (key >= kend || (a.causal && key > qpos)) sacc[u][r] = -INFINITY;
+        }
       }
-    }
-    float mloc = sacc[0];
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mloc = fmaxf(mloc, sacc[r]);
+      for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[u][r]);
+    }
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32, WAVE)) * scale;
     // Lazy rescaling: the exponent reference m_run only moves when some query of
     // the wavefront sees a score more than 2^RESCALE above it (then all lanes
-    // rescale together); otherwise p <= 2^RESCALE and the output accumulators,
-    // which live in AGPRs, are not touched.  o / l is unchanged by the choice.
+    // rescale together); otherwise p <= 2^RESCALE and the output accumulators
+    // are not touched.  o / l is unchanged by the choice.
     if (__any(mloc > m_run + RESCALE)) {
       const float m_new = fmaxf(m_run, mloc);
       const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
@@ -267,52 +279,60 @@ __global__ void __launch_bounds__(GS * 64) k_attn(AttnArgs a, int chunk_len) {
     }
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
     float lsum = 0.f;
+    bf16x8 pb[SUB][2];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(sacc[r], scale, -m_use));
-      sacc[r] = p;
-      lsum += p;
+    for (int u = 0; u < SUB; ++u) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[u][r], scale, -m_use));
+        sacc[u][r] = p;
+        lsum += p;
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        u32x4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = pack_bf16x2(sacc[u][8 * c + 2 * e], sacc[u][8 * c + 2 * e + 1]);
+        pb[u][c] = as_bf16x8(x);
+      }
     }
     lsum += __shfl_xor(lsum, 32, WAVE);
     l_run += lsum;
-    bf16x8 pb[2];
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      u32x4 u;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) u[e] = pack_bf16x2(sacc[8 * c + 2 * e], sacc[8 * c + 2 * e + 1]);
-      pb[c] = as_bf16x8(u);
-    }
-    // cache slots past the row's end may hold anything (also NaN): their values
-    // are zeroed in the fragments, not only their probabilities
+    // cache slots past the row's end may hold anything (also NaN), and a tile
+    // past the range was not loaded: their values are zeroed in the fragments,
+    // not only their probabilities
     constexpr int DH = ND > 1 ? ND / 2 : 1;  // output blocks per batch of V reads
 #pragma unroll
     for (int d0 = 0; d0 < ND; d0 += DH) {
-      uint32_t va[2 * DH];
-      u32x4 vf[2 * DH];
+      uint32_t va[SUB * 2 * DH];
+      u32x4 vf[SUB * 2 * DH];
 #pragma unroll
-      for (int dd = 0; dd < DH; ++dd)
+      for (int u = 0; u < SUB; ++u)
 #pragma unroll
-        for (int c = 0; c < 2; ++c) va[2 * dd + c] = sb + voff + c * (HD * 32) + (d0 + dd) * 1024;
-      lds_read_n<2 * DH>(va, vf);
+        for (int dd = 0; dd < DH; ++dd)
 #pragma unroll
-      for (int dd = 0; dd < DH; ++dd)
+          for (int c = 0; c < 2; ++c)
+            va[(u * DH + dd) * 2 + c] = sb + u * TILE + voff + c * (HD * 32) + (d0 + dd) * 1024;
+      lds_read_n<SUB * 2 * DH>(va, vf);
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int dc = d0 + dd;
-        u32x4 x4 = vf[2 * dd + c];
-        if (tail) {
-          const int valid = kend - (k0 + 16 * c + 8 * half);  // keys of this fragment still in range
+      for (int u = 0; u < SUB; ++u)
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            uint32_t x = x4[u];
-            if (2 * u >= valid) x &= 0xffff0000u;
-            if (2 * u + 1 >= valid) x &= 0x0000ffffu;
-            x4[u] = x;
+        for (int dd = 0; dd < DH; ++dd)
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            u32x4 x4 = vf[(u * DH + dd) * 2 + c];
+            if (tail[u]) {
+              const int valid = kend - (k0 + u * KT + 16 * c + 8 * half);  // keys of this fragment in range
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                uint32_t x = x4[e];
+                if (2 * e >= valid) x &= 0xffff0000u;
+                if (2 * e + 1 >= valid) x &= 0x0000ffffu;
+                x4[e] = x;
+              }
+            }
+            o[d0 + dd] = mfma32x32x16(as_bf16x8(x4), pb[u][c], o[d0 + dd]);
           }
-        }
-        o[dc] = mfma32x32x16(as_bf16x8(x4), pb[c], o[dc]);
-      }
     }
   }
 
@@ -415,7 +435,7 @@ static hipError_t launch(const AttnArgs& a, hipStream_t s) {
   const int splits = attn_splits(a, &chunk);
   const int qblocks = (a.Lq + 31) / 32;
   dim3 grid(splits, qblocks, a.B * a.G);
-  hipLaunchKernelGGL((k_attn<HD, GS, ATT_STAGES>), grid, dim3(GS * 64), 0, s, a, chunk);
+  hipLaunchKernelGGL((k_attn<HD, GS>), grid, dim3(GS * 64), 0, s, a, chunk);
   if (splits > 1) {
     const int pairs = a.B * a.Lq * a.H;
     hipLaunchKernelGGL((k_attn_merge<HD>), dim3((pairs + 3) / 4), dim3(256), 0, s, a, splits);
