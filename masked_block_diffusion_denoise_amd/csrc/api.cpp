@@ -200,11 +200,26 @@ dlm_status run_layers(const dlm_model* m, const dlm_kv* kv, const int32_t* token
   DLM_TRY(embed_norm(tokens, R, Lq, tok_ld, m->embed, c.vocab, d, m->attn_norm[0], c.rms_eps, p.x, p.xn,
                      flags ? flags + 1 : nullptr, prefix, pos_offset, c.head_dim, c.rope_base, p.tab, s),
           "embed_norm");
+  // x += A W^T; with gain, then xn = RMSNorm(x) * gain.  Short products split
+  // over K fuse their reduction with the norm (one kernel instead of two).
+  auto resid_gemm = [&](const GemmArgs& g, const void* gain, const char* what) -> dlm_status {
+    const int S = gemm_ksplit(g.M, g.N, g.K);
+    if (gain && S > 1 && g.alpha == 1.f) {
+      DLM_TRY(gemm_partials(g, s), what);
+      DLM_TRY(resid_norm(p.kpart, S, R, p.x, d, gain, c.rms_eps, p.xn, s), "residual + rmsnorm");
+      return DLM_OK;
+    }
+    DLM_TRY(gemm(g, EPI_RESID_F32, s), what);
+    if (gain) DLM_TRY(rmsnorm(p.x, R, d, gain, c.rms_eps, p.xn, nullptr, nullptr, s), "rmsnorm");
+    return DLM_OK;
+  };
   const size_t lkv = layer_kv_elems(c, kv);
+  dlm_status st;
   for (int l = 0; l < c.n_layers; ++l) {
     bf16_t* kc = static_cast<bf16_t*>(kv->k) + l * lkv;
     bf16_t* vc = static_cast<bf16_t*>(kv->v) + l * lkv;
-    if (l > 0) DLM_TRY(rmsnorm(p.x, R, d, m->attn_norm[l], c.rms_eps, p.xn, nullptr, nullptr, s), "rmsnorm");
+    // p.xn holds RMSNorm(x) * attn_norm[l]: from embed_norm (layer 0) or the
+    // previous layer's down projection
     GemmArgs g{};
     g.kpart = p.kpart;
     g.a = p.xn;
@@ -215,13 +230,24 @@ dlm_status run_layers(const dlm_model* m, const dlm_kv* kv, const int32_t* token
     g.K = d;
     g.lda = d;
     g.ldc = nq;
-    {
+    // short products split over K sum their partials inside the RoPE + cache
+    // write (the QKV timer then covers that kernel too)
+    const int qs = gemm_ksplit(R, nq, d);
+    if (qs > 1) {
       TimerScope t(DLM_TIMER_QKV, s, l == 0);
-      DLM_TRY(gemm(g, EPI_STORE_BF16, s), "gemm qkv");
+      DLM_TRY(gemm_partials(g, s), "gemm qkv");
+      DLM_TRY(rope_kv(p.qkv, R, Lq, c.n_heads, c.n_kv_heads, c.head_dim, p.tab, kc, vc, prefix, pos_offset,
+                      kv->capacity, s, p.kpart, qs),
+              "rope_kv");
+    } else {
+      {
+        TimerScope t(DLM_TIMER_QKV, s, l == 0);
+        DLM_TRY(gemm(g, EPI_STORE_BF16, s), "gemm qkv");
+      }
+      DLM_TRY(rope_kv(p.qkv, R, Lq, c.n_heads, c.n_kv_heads, c.head_dim, p.tab, kc, vc, prefix, pos_offset,
+                      kv->capacity, s),
+              "rope_kv");
     }
-    DLM_TRY(rope_kv(p.qkv, R, Lq, c.n_heads, c.n_kv_heads, c.head_dim, p.tab, kc, vc, prefix, pos_offset,
-                    kv->capacity, s),
-            "rope_kv");
     AttnArgs a{};
     a.q = p.qkv;
     a.ldq = nq;
@@ -251,8 +277,8 @@ dlm_status run_layers(const dlm_model* m, const dlm_kv* kv, const int32_t* token
     g.K = qd;
     g.lda = qd;
     g.ldc = d;
-    DLM_TRY(gemm(g, EPI_RESID_F32, s), "gemm o");
-    if (m->lora_on) {  // x += scale * (o A^T) B^T
+    if ((st = resid_gemm(g, m->lora_on ? nullptr : m->ffn_norm[l], "gemm o")) != DLM_OK) return st;
+    if (m->lora_on) {  // x += scale * (o A^T) B^T, then the FFN norm
       GemmArgs la{};
       la.kpart = p.kpart;
       la.a = p.attn;
@@ -272,9 +298,8 @@ dlm_status run_layers(const dlm_model* m, const dlm_kv* kv, const int32_t* token
       la.lda = m->lora_rank;
       la.ldc = d;
       la.alpha = m->lora_scale;
-      DLM_TRY(gemm(la, EPI_RESID_F32, s), "gemm lora b");
+      if ((st = resid_gemm(la, m->ffn_norm[l], "gemm lora b")) != DLM_OK) return st;
     }
-    DLM_TRY(rmsnorm(p.x, R, d, m->ffn_norm[l], c.rms_eps, p.xn, nullptr, nullptr, s), "rmsnorm");
     g.a = p.xn;
     g.w = m->wgu[l];
     g.out = p.u;
@@ -294,8 +319,10 @@ dlm_status run_layers(const dlm_model* m, const dlm_kv* kv, const int32_t* token
     g.lda = c.d_ffn;
     g.ldc = d;
     {
+      // with the next layer's attention norm (the last layer's final norm is the caller's)
       TimerScope t(DLM_TIMER_DOWN, s, l == 0);
-      DLM_TRY(gemm(g, EPI_RESID_F32, s), "gemm down");
+      if ((st = resid_gemm(g, l + 1 < c.n_layers ? m->attn_norm[l + 1] : nullptr, "gemm down")) != DLM_OK)
+        return st;
     }
   }
   return DLM_OK;

@@ -44,6 +44,27 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Sum of S <= SPLIT_MAX fp32 partial planes at p, p + plane, ... (split order).
+// Every load is issued before the first add, so the S reads overlap instead of
+// each waiting for the previous sum (S is uniform across the wavefront).
+constexpr int SPLIT_MAX = 8;
+__device__ __forceinline__ float4 sum_planes(const float* p, size_t plane, int S) {
+  float4 a[SPLIT_MAX];
+#pragma unroll
+  for (int k = 0; k < SPLIT_MAX; ++k)
+    if (k < S) a[k] = *reinterpret_cast<const float4*>(p + k * plane);
+  float4 acc = a[0];
+#pragma unroll
+  for (int k = 1; k < SPLIT_MAX; ++k)
+    if (k < S) {
+      acc.x += a[k].x;
+      acc.y += a[k].y;
+      acc.z += a[k].z;
+      acc.w += a[k].w;
+    }
+  return acc;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);

@@ -48,6 +48,10 @@ int gemm_head_tile_n(int M);                       // vocab columns per EPI_HEAD
 int gemm_ksplit(int M, int N, int K);
 size_t gemm_workspace_bytes(int M, int N, int K);
 hipError_t gemm(const GemmArgs& g, GemmEpilogue epi, hipStream_t s);
+// Only the K-split partial products, fp32 [S][M][N] into g.kpart, with
+// S = gemm_ksplit(M, N, K) > 1 (else an error): for callers that fuse the
+// reduction into the next step (resid_norm, rope_kv).
+hipError_t gemm_partials(const GemmArgs& g, hipStream_t s);
 
 // --------------------------------------------------------- attention ----
 struct AttnArgs {
@@ -83,8 +87,15 @@ hipError_t rmsnorm(const float* x, int M, int d, const void* gain, float eps, vo
                    const int* rows, const int* m_dev, hipStream_t s);
 hipError_t rope_table(const int* prefix, int pos_offset, int B, int Lq, int hd, float base, float2* tab,
                       hipStream_t s);
+// part (with S splits): the row values are the sum of fp32 K-split partials
+// [S][M][(H+2G)hd] instead of bf16 qkv
 hipError_t rope_kv(void* qkv, int M, int Lq, int H, int G, int hd, const float2* tab, void* kc, void* vc,
-                   const int* prefix, int pos_offset, int cap, hipStream_t s);
+                   const int* prefix, int pos_offset, int cap, hipStream_t s, const float* part = nullptr,
+                   int S = 1);
+// x[m] += sum_s part[s][m] over S fp32 partial planes [S][M][d], then
+// xn[m] = RMSNorm(x[m]) * gain (bf16)
+hipError_t resid_norm(const float* part, int S, int M, float* x, int d, const void* gain, float eps, void* xn,
+                      hipStream_t s);
 // rows[0..count) = indices m with masked[m] != 0, ascending, and count[0] = how
 // many, fused with the final RMSNorm of those rows into xn[0..count)
 hipError_t masked_norm(const uint8_t* masked, int M, const float* x, int d, const void* gain, float eps, void* xn,

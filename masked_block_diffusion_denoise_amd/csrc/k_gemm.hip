@@ -429,22 +429,13 @@ __global__ void __launch_bounds__(256) k_splitk_reduce(GemmArgs g) {
     // output column c of a 16-column group reads gate row 32*(c/16) + c%16 and
     // the up row 16 further (gate/up rows interleaved by 16)
     const int n = 32 * (c / 16) + c % 16;
-    float4 gs = make_float4(0.f, 0.f, 0.f, 0.f), us = gs;
-    for (int k = 0; k < g.ksplit; ++k) {
-      const float4 a = *reinterpret_cast<const float4*>(row + k * plane + n);
-      const float4 b = *reinterpret_cast<const float4*>(row + k * plane + n + 16);
-      gs.x += a.x; gs.y += a.y; gs.z += a.z; gs.w += a.w;
-      us.x += b.x; us.y += b.y; us.z += b.z; us.w += b.w;
-    }
+    const float4 gs = sum_planes(row + n, plane, g.ksplit), us = sum_planes(row + n + 16, plane, g.ksplit);
     bf16_t* o = static_cast<bf16_t*>(g.out) + static_cast<size_t>(m) * g.ldc + c;
     *reinterpret_cast<u32x2*>(o) = u32x2{pack_bf16x2(silu_f(gs.x) * us.x, silu_f(gs.y) * us.y),
                                          pack_bf16x2(silu_f(gs.z) * us.z, silu_f(gs.w) * us.w)};
   } else {
-    float v[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < g.ksplit; ++k) {
-      const float4 a = *reinterpret_cast<const float4*>(row + k * plane + c);
-      v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
-    }
+    const float4 a = sum_planes(row + c, plane, g.ksplit);
+    float v[4] = {a.x, a.y, a.z, a.w};
     store_quad<EPI>(g, m, c, v);
   }
 }
@@ -465,7 +456,7 @@ int gemm_ksplit(int M, int N, int K) {
   if (M > SK_BM) return 1;
   const int tiles = N / SK_BN;
   const int want = (640 + tiles - 1) / tiles;
-  return std::max(1, std::min({want, K / (16 * TL_BK), 8}));
+  return std::max(1, std::min({want, K / (16 * TL_BK), SPLIT_MAX}));
 }
 
 size_t gemm_workspace_bytes(int M, int N, int K) {
@@ -530,6 +521,15 @@ static hipError_t launch_epi(const GemmArgs& g, hipStream_t s) {
     else
       launch_tiled<EPI, 128, 128, 2, 2, 4>(g, s);
   }
+  return hipGetLastError();
+}
+
+hipError_t gemm_partials(const GemmArgs& g, hipStream_t s) {
+  const int S = gemm_ksplit(g.M, g.N, g.K);
+  if (g.M <= 0 || S <= 1 || !g.kpart) return hipErrorInvalidValue;
+  GemmArgs h = g;
+  h.ksplit = S;
+  launch_tiled<EPI_SPLITK, SK_BN, SK_BM, 4, 1, 3, 64>(h, s);
   return hipGetLastError();
 }
 

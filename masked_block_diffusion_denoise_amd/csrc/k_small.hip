@@ -196,6 +196,54 @@ __global__ void __launch_bounds__(256) k_rmsnorm(const float* __restrict__ x, in
   }
 }
 
+// Residual update from K-split partials fused with the next RMSNorm:
+// x[m] += sum_s part[s][m] (split order), then xn[m] = RMSNorm(x[m]) * g.  One
+// block per row; a thread re-reads only the x values it wrote itself.
+__global__ void __launch_bounds__(256) k_resid_norm(const float* __restrict__ part, int S, int M,
+                                                    float* __restrict__ x, int d, const bf16_t* __restrict__ g,
+                                                    float eps, bf16_t* __restrict__ xn) {
+  __shared__ float red[4];
+  const int m = blockIdx.x;
+  const size_t plane = static_cast<size_t>(M) * d;
+  float* xr = x + static_cast<size_t>(m) * d;
+  const float* pr = part + static_cast<size_t>(m) * d;
+  float ss = 0.f;
+  for (int c = threadIdx.x; c < d / 8; c += 256) {
+    float4 v0 = reinterpret_cast<const float4*>(xr)[2 * c];
+    float4 v1 = reinterpret_cast<const float4*>(xr)[2 * c + 1];
+    const float4 a0 = sum_planes(pr + 8 * c, plane, S);
+    const float4 a1 = sum_planes(pr + 8 * c + 4, plane, S);
+    v0.x += a0.x; v0.y += a0.y; v0.z += a0.z; v0.w += a0.w;
+    v1.x += a1.x; v1.y += a1.y; v1.z += a1.z; v1.w += a1.w;
+    reinterpret_cast<float4*>(xr)[2 * c] = v0;
+    reinterpret_cast<float4*>(xr)[2 * c + 1] = v1;
+    ss += v0.x * v0.x + v0.y * v0.y + v0.z * v0.z + v0.w * v0.w + v1.x * v1.x + v1.y * v1.y + v1.z * v1.z +
+          v1.w * v1.w;
+  }
+  const float rstd = rsqrtf(block_sum_256(ss, red) / d + eps);
+  for (int c = threadIdx.x; c < d / 8; c += 256) {
+    const float4 v0 = reinterpret_cast<const float4*>(xr)[2 * c];
+    const float4 v1 = reinterpret_cast<const float4*>(xr)[2 * c + 1];
+    float gg[8];
+    unpack8(ld16(g + c * 8), gg);
+    u32x4 o;
+    o[0] = pack_bf16x2(v0.x * rstd * gg[0], v0.y * rstd * gg[1]);
+    o[1] = pack_bf16x2(v0.z * rstd * gg[2], v0.w * rstd * gg[3]);
+    o[2] = pack_bf16x2(v1.x * rstd * gg[4], v1.y * rstd * gg[5]);
+    o[3] = pack_bf16x2(v1.z * rstd * gg[6], v1.w * rstd * gg[7]);
+    st16(xn + static_cast<size_t>(m) * d + c * 8, o);
+  }
+}
+
+hipError_t resid_norm(const float* part, int S, int M, float* x, int d, const void* gain, float eps, void* xn,
+                      hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  if (S < 1 || S > SPLIT_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_resid_norm, dim3(M), dim3(256), 0, s, part, S, M, x, d, static_cast<const bf16_t*>(gain),
+                     eps, static_cast<bf16_t*>(xn));
+  return hipGetLastError();
+}
+
 hipError_t rmsnorm(const float* x, int M, int d, const void* gain, float eps, void* xn, const int* rows,
                    const int* m_dev, hipStream_t s) {
   if (M <= 0) return hipSuccess;
@@ -218,12 +266,17 @@ hipError_t rope_table(const int* prefix, int pos_offset, int B, int Lq, int hd, 
   return hipGetLastError();
 }
 
-// Rotate the query heads in place and write the rotated keys and the values of
-// every row into the cache slot of its position.  qkv row layout: H query heads,
-// then G key heads, then G value heads, each hd wide.  Each thread handles four
-// rotation pairs of one head.  K cache [B][G][cap][hd]; V cache
-// [B][G][cap/16][hd][16] (blocks of 16 positions, position fastest).
-__global__ void __launch_bounds__(256) k_rope_kv(bf16_t* __restrict__ qkv, int Lq, int H, int G, int hd,
+// Rotate the query heads and write the rotated keys and the values of every row
+// into the cache slot of its position.  qkv row layout: H query heads, then G
+// key heads, then G value heads, each hd wide.  The row's values come either
+// from bf16 qkv (rotated query heads are written back in place) or, with PART,
+// from fp32 K-split partials [S][M][(H+2G)hd] summed in split order (the query
+// heads are then written to qkv, rounded to bf16 once, after the rotation).
+// Each thread handles four rotation pairs of one head.  K cache [B][G][cap][hd];
+// V cache [B][G][cap/16][hd][16] (blocks of 16 positions, position fastest).
+template <bool PART>
+__global__ void __launch_bounds__(256) k_rope_kv(bf16_t* __restrict__ qkv, const float* __restrict__ part, int S,
+                                                 int M, int Lq, int H, int G, int hd,
                                                  const float2* __restrict__ tab, bf16_t* __restrict__ kc,
                                                  bf16_t* __restrict__ vc, const int* __restrict__ prefix,
                                                  int off, int cap) {
@@ -234,26 +287,40 @@ __global__ void __launch_bounds__(256) k_rope_kv(bf16_t* __restrict__ qkv, int L
   const int pos = (prefix ? prefix[b] : 0) + off + j;
   const bool slot_ok = pos >= 0 && pos < cap;
   bf16_t* row = qkv + static_cast<size_t>(m) * nh * hd;
-  for (int t = threadIdx.x; t < nh * quads; t += blockDim.x) {
+  const size_t plane = static_cast<size_t>(M) * nh * hd;
+  const float* prow = PART ? part + static_cast<size_t>(m) * nh * hd : nullptr;
+  // four consecutive values of the row from column c
+  auto load4 = [&](int c, float* v) {
+    if constexpr (PART) {
+      const float4 acc = sum_planes(prow + c, plane, S);
+      v[0] = acc.x; v[1] = acc.y; v[2] = acc.z; v[3] = acc.w;
+    } else {
+      const u32x2 u = *reinterpret_cast<const u32x2*>(row + c);
+      v[0] = __uint_as_float(u[0] << 16);
+      v[1] = __uint_as_float(u[0] & 0xffff0000u);
+      v[2] = __uint_as_float(u[1] << 16);
+      v[3] = __uint_as_float(u[1] & 0xffff0000u);
+    }
+  };
+  // one (head, quad) task per thread; blockIdx.y picks 256 of the row's tasks
+  {
+    const int t = blockIdx.y * blockDim.x + threadIdx.x;
+    if (t >= nh * quads) return;
     const int h = t / quads, i0 = (t % quads) * 4;
-    bf16_t* hp = row + h * hd;
-    if (h >= H + G) {  // value head: copy to the blocked V cache
-      if (!slot_ok) continue;
+    float x1[4], x2[4];
+    load4(h * hd + i0, x1);
+    load4(h * hd + i0 + half, x2);
+    if (h >= H + G) {  // value head: to the blocked V cache
+      if (!slot_ok) return;
       const int g = h - H - G;
       bf16_t* vb = vc + ((static_cast<size_t>(b) * G + g) * (cap / 16) + pos / 16) * hd * 16 + pos % 16;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        vb[(i0 + u) * 16] = hp[i0 + u];
-        vb[(i0 + u + half) * 16] = hp[i0 + u + half];
+        vb[(i0 + u) * 16] = f32_to_bf16(x1[u]);
+        vb[(i0 + u + half) * 16] = f32_to_bf16(x2[u]);
       }
-      continue;
+      return;
     }
-    const u32x2 lo = *reinterpret_cast<const u32x2*>(hp + i0);
-    const u32x2 hi = *reinterpret_cast<const u32x2*>(hp + i0 + half);
-    float x1[4] = {__uint_as_float(lo[0] << 16), __uint_as_float(lo[0] & 0xffff0000u),
-                   __uint_as_float(lo[1] << 16), __uint_as_float(lo[1] & 0xffff0000u)};
-    float x2[4] = {__uint_as_float(hi[0] << 16), __uint_as_float(hi[0] & 0xffff0000u),
-                   __uint_as_float(hi[1] << 16), __uint_as_float(hi[1] & 0xffff0000u)};
     float y1[4], y2[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -264,6 +331,7 @@ __global__ void __launch_bounds__(256) k_rope_kv(bf16_t* __restrict__ qkv, int L
     const u32x2 olo = {pack_bf16x2(y1[0], y1[1]), pack_bf16x2(y1[2], y1[3])};
     const u32x2 ohi = {pack_bf16x2(y2[0], y2[1]), pack_bf16x2(y2[2], y2[3])};
     if (h < H) {
+      bf16_t* hp = row + h * hd;
       *reinterpret_cast<u32x2*>(hp + i0) = olo;
       *reinterpret_cast<u32x2*>(hp + i0 + half) = ohi;
     } else if (slot_ok) {
@@ -276,10 +344,16 @@ __global__ void __launch_bounds__(256) k_rope_kv(bf16_t* __restrict__ qkv, int L
 }
 
 hipError_t rope_kv(void* qkv, int M, int Lq, int H, int G, int hd, const float2* tab, void* kc, void* vc,
-                   const int* prefix, int pos_offset, int cap, hipStream_t s) {
+                   const int* prefix, int pos_offset, int cap, hipStream_t s, const float* part, int S) {
   if (M <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_rope_kv, dim3(M), dim3(256), 0, s, static_cast<bf16_t*>(qkv), Lq, H, G, hd, tab,
-                     static_cast<bf16_t*>(kc), static_cast<bf16_t*>(vc), prefix, pos_offset, cap);
+  if (part && (S < 1 || S > SPLIT_MAX)) return hipErrorInvalidValue;
+  const dim3 grid(M, ((H + 2 * G) * (hd / 8) + 255) / 256);
+  if (part)
+    hipLaunchKernelGGL(k_rope_kv<true>, grid, dim3(256), 0, s, static_cast<bf16_t*>(qkv), part, S, M, Lq, H, G,
+                       hd, tab, static_cast<bf16_t*>(kc), static_cast<bf16_t*>(vc), prefix, pos_offset, cap);
+  else
+    hipLaunchKernelGGL(k_rope_kv<false>, grid, dim3(256), 0, s, static_cast<bf16_t*>(qkv), nullptr, 1, M, Lq, H,
+                       G, hd, tab, static_cast<bf16_t*>(kc), static_cast<bf16_t*>(vc), prefix, pos_offset, cap);
   return hipGetLastError();
 }
 

@@ -237,3 +237,70 @@ def test_layer8b_append_block_batch1(layer8b):
         top2 = np.sort(lo[j][np.isfinite(lo[j])])[-2:]
         if top2[1] - top2[0] > 5e-2:
             assert host(arg)[0, j] == arg_o[j], j
+
+
+# Two layers wide enough (d 1024) that the batch-1 projections split over K:
+# the partial sums fold into RoPE + KV write and into the residual add + the
+# next RMSNorm (after the output projection and after the down projection,
+# which normalises for the next layer).
+WIDE2 = synth.ModelShape(n_layers=2, d_model=1024, n_heads=8, n_kv_heads=2, head_dim=128, d_ffn=2048,
+                         vocab=2048, mask_id=0, rope_base=1.0e6)
+
+
+def test_two_wide_layers_split_reductions_prefill_denoise_append():
+    announce("two wide layers: K-split reductions fused")
+    shape = WIDE2
+    # head gain 2: logit spread ~1.3 as for the 8B-class head at unit gain (a
+    # larger gain pushes confidences near 1, where the bf16 logit error alone
+    # moves them by ~1e-2)
+    w = synth.model_weights(shape, seed=4, lm_head_gain=2.0)
+    m = make(shape, w)
+    T, Lb = 40, 32
+    prompt = synth.prompt(shape, 1, T, seed=6)
+    sess = R.Session(m, 1, 128, Lb)
+    sess.prefill(i32(prompt))
+    cache, _ = oracle.prefill(w, shape, prompt[0])
+    sync()
+    for layer in range(shape.n_layers):
+        kg = host(sess.kv.k_logical()[layer, 0, :, :T].float())
+        vg = host(sess.kv.v_logical()[layer, 0, :, :T].float())
+        assert rel_rms(kg, cache.k[layer][:, :T]) < 1e-2, layer
+        assert rel_rms(vg, cache.v[layer][:, :T]) < 1e-2, layer
+
+    canvas, masked = synth.ragged_canvas(shape, 1, Lb, seed=6)
+    sess.canvas.copy_(i32(canvas))
+    sess.masked.copy_(u8(masked))
+    logits = torch.zeros(Lb, shape.vocab, dtype=torch.float32, device="cuda")
+    sess.denoise_step(logits)
+    sync()
+    lo = oracle.denoise_logits(w, shape, cache, canvas[0])
+    conf_o, arg_o = oracle.confidence(lo)
+    lg = host(logits)
+    mk = np.flatnonzero(masked[0])
+    assert np.abs(host(sess.conf)[0, mk] - conf_o[mk]).max() < 1e-2
+    for j in mk:
+        fin = np.isfinite(lo[j])
+        assert rel_rms(lg[j][fin], lo[j][fin]) < 2e-2, j
+        top2 = np.sort(lo[j][fin])[-2:]
+        if top2[1] - top2[0] > 5e-2:
+            assert host(sess.argmax)[0, j] == arg_o[j], j
+
+    block = synth.prompt(shape, 1, Lb, seed=7)
+    arg = torch.zeros(1, Lb, dtype=torch.int32, device="cuda")
+    conf = torch.zeros(1, Lb, dtype=torch.float32, device="cuda")
+    sess.append(i32(block), arg, conf)
+    x = oracle.append_block(w, shape, cache, block[0])
+    sync()
+    for layer in range(shape.n_layers):
+        kg = host(sess.kv.k_logical()[layer, 0, :, T:T + Lb].float())
+        vg = host(sess.kv.v_logical()[layer, 0, :, T:T + Lb].float())
+        assert rel_rms(kg, cache.k[layer][:, T:T + Lb]) < 1e-2, layer
+        assert rel_rms(vg, cache.v[layer][:, T:T + Lb]) < 1e-2, layer
+    lo = oracle.head_logits(w, shape, x)
+    conf_o, arg_o = oracle.confidence(lo)
+    assert np.abs(host(conf)[0] - conf_o).max() < 1e-2
+    for j in range(Lb):
+        top2 = np.sort(lo[j][np.isfinite(lo[j])])[-2:]
+        if top2[1] - top2[0] > 5e-2:
+            assert host(arg)[0, j] == arg_o[j], j
+    assert (host(sess.flags) == 0).all()
