@@ -30,6 +30,12 @@ Pins (what each function is checked against, in tests/test_oracle_*.py):
                              quota 1 takes L steps; all-confident takes 1),
                              never-remask, forced completion, worked example A
   generate_ar                equals recompute-from-scratch causal argmax decoding
+  entropy                    uniform over the V-1 non-mask ids is ln(V-1), a
+                             two-way split is the binary entropy, one dominant
+                             logit tends to 0
+  commit_rule, adaptive_stop hand-worked cases from the page statements
+                             (tests/golden/sampler_rules.json), the native rule
+                             equal to ``commit``, brute force over tiny cases
   generate_linear_spec       equals generate_ar token for token (lossless), with
                              and without the adaptive window; its trimmed cache
                              equals a causal prefill of prompt + output
@@ -37,16 +43,18 @@ Whole-model numeric values of a random-init network are not printed on any
 page: beyond the pins above, those are "parity unpinned" (self-consistency only).
 """
 from .model import (KVCache, rms_norm, rope, attend, forward, head_logits,
-                    confidence, silu)
+                    confidence, entropy, silu)
 from .decode import (commit, commit_batch, linear_mask_schedule, sample_fixed_schedule,
                      generate_block_diffusion, generate_ar, generate_ar_recompute,
                      denoise_logits, append_block, prefill, BlockStats,
-                     generate_linear_spec, next_draft_window)
+                     generate_linear_spec, next_draft_window, commit_rule, adaptive_stop,
+                     commit_ex, RULES)
 
 __all__ = [
     "KVCache", "rms_norm", "rope", "attend", "forward", "head_logits", "confidence",
     "silu", "commit", "commit_batch", "linear_mask_schedule", "sample_fixed_schedule",
     "generate_block_diffusion", "generate_ar", "generate_ar_recompute",
     "denoise_logits", "append_block", "prefill", "BlockStats",
-    "generate_linear_spec", "next_draft_window",
+    "generate_linear_spec", "next_draft_window", "entropy", "commit_rule", "adaptive_stop",
+    "commit_ex", "RULES",
 ]

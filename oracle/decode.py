@@ -75,6 +75,128 @@ def commit_batch(conf, argmax, canvas, masked, tau, quota, steps, max_steps):
             masked_new.sum(axis=1))
 
 
+# ------------------------------------------------------ sampler variants ----
+# The other samplers of the pages, as commit rules of one row.  Where the GPU
+# decides an integer from float32 values (a threshold test, a cumulative sum, a
+# mean), the same float32 operations are done here in the same order, on the
+# float32 inputs both sides are given.
+RULES = ("threshold", "bound", "entropy")
+F32 = np.float32
+
+
+def _bound_threshold(j, scaling):
+    """Position-dependent threshold 1 - scaling / (j + 2) of the bounded sampler, in float32."""
+    return F32(1.0) - F32(scaling) / F32(j + 2)
+
+
+def commit_rule(conf, argmax, canvas, masked, tau, quota, step, max_steps, rule="threshold",
+                min_threshold=0.45, scaling=2.0, entropy=None, entropy_bound=0.1, max_transfer=0):
+    """Commit rules of the samplers on the pages, one row; returns
+    (canvas, masked, step, n_committed) like ``commit``.
+
+    rule "threshold" (native; MLX guide sec. 5.2): A = {masked j : conf_j > tau}.
+    rule "bound" (confidence_threshold_bound; MLX guide sec. 5.2): a position
+      qualifies when its confidence reaches the global threshold, conf_j >= tau,
+      or is at least min_threshold (0.45) and at least the position-dependent
+      threshold 1 - scaling / (j + 2) (scaling 2.0); j is the position in the
+      block (a reading: the page names the position without its origin).
+    rule "entropy" (EntropyBoundScheduler; DiffusionGemma docs, Schedulers):
+      masked positions in order of (entropy, position); A is the longest prefix
+      whose cumulative entropy (float32, in that order) stays <= entropy_bound.
+    Then, as for the native rule: on the last allowed step every remaining mask
+    is committed; otherwise at least q = min(quota, #masked) positions open --
+    A when |A| >= q, else A plus the best-ranked others -- and with
+    max_transfer > 0 (MLX guide sec. 5.5, --max-transfer-per-step) at most that
+    many, the best-ranked of the chosen.  Ranking: (-conf, position) for the
+    confidence rules, (entropy, position) for the entropy rule.
+    """
+    if rule not in RULES:
+        raise ValueError(f"unknown rule {rule!r}")
+    canvas = np.array(canvas, copy=True)
+    masked = np.array(masked, dtype=bool, copy=True)
+    idx = np.flatnonzero(masked).tolist()
+    if not idx:
+        return canvas, masked, step, 0
+    conf = np.asarray(conf, dtype=F32)
+    if rule == "entropy":
+        if entropy is None:
+            raise ValueError("the entropy rule needs per-position entropies")
+        ent = np.asarray(entropy, dtype=F32)
+        key = lambda j: (float(ent[j]), j)
+    else:
+        key = lambda j: (-float(conf[j]), j)
+    ranked = sorted(idx, key=key)
+    if step >= max_steps - 1:
+        chosen = ranked                      # forced completion
+    else:
+        if rule == "threshold":
+            A = [j for j in ranked if conf[j] > F32(tau)]
+        elif rule == "bound":
+            A = [j for j in ranked if conf[j] >= F32(tau) or
+                 (conf[j] >= F32(min_threshold) and conf[j] >= _bound_threshold(j, scaling))]
+        else:
+            A, total = [], F32(0.0)
+            for j in ranked:
+                total = F32(total + ent[j])
+                if total > F32(entropy_bound):
+                    break
+                A.append(j)
+        q = min(int(quota), len(idx))
+        chosen = A + [j for j in ranked if j not in A][:max(0, q - len(A))]
+        if max_transfer > 0 and len(chosen) > max_transfer:
+            chosen = sorted(chosen, key=key)[:max_transfer]
+    for j in chosen:
+        canvas[j] = argmax[j]
+        masked[j] = False
+    return canvas, masked, step + 1, len(chosen)
+
+
+def adaptive_stop(argmax, prev_argmax, masked, entropy, stable, stability_steps, stop_entropy):
+    """Adaptive stopping of one row (DiffusionGemma docs, adaptive stopping).
+
+    ``stable`` counts the consecutive steps whose argmax at every masked
+    position equals the previous step's (prev_argmax; -1 before the first step
+    of a block).  The row stops when that count reaches stability_steps and the
+    mean entropy of its masked positions (float32 sum in position order, then
+    the division) is below stop_entropy (0.005 for the published checkpoint);
+    a stopped row commits every remaining mask with its argmax (a reading: the
+    page freezes the sample's current predictions).  Returns (stop, stable).
+    """
+    idx = np.flatnonzero(np.asarray(masked, dtype=bool))
+    if idx.size == 0:
+        return False, stable
+    same = all(int(argmax[j]) == int(prev_argmax[j]) for j in idx)
+    stable = stable + 1 if same else 0
+    total = F32(0.0)
+    for j in idx:
+        total = F32(total + F32(entropy[j]))
+    mean = F32(total / F32(idx.size))
+    return bool(stable >= stability_steps and mean < F32(stop_entropy)), stable
+
+
+def commit_ex(conf, argmax, canvas, masked, tau, quota, step, max_steps, entropy=None,
+              prev_argmax=None, stable=0, stability_steps=0, stop_entropy=0.005, **rule_kw):
+    """``commit_rule`` preceded by adaptive stopping when stability_steps > 0.
+
+    Returns (canvas, masked, step, n_committed, prev_argmax, stable): prev_argmax
+    takes this step's argmax at the positions that were masked.
+    """
+    masked = np.asarray(masked, dtype=bool)
+    if stability_steps > 0:
+        stop, stable = adaptive_stop(argmax, prev_argmax, masked, entropy, stable, stability_steps,
+                                     stop_entropy)
+        prev_argmax = np.array(prev_argmax, copy=True)
+        prev_argmax[masked] = np.asarray(argmax)[masked]
+        if stop:
+            idx = np.flatnonzero(masked)
+            canvas = np.array(canvas, copy=True)
+            canvas[idx] = np.asarray(argmax)[idx]
+            return canvas, np.zeros_like(masked), step + 1, int(idx.size), prev_argmax, stable
+    c, m, s, n = commit_rule(conf, argmax, canvas, masked, tau, quota, step, max_steps, entropy=entropy,
+                             **rule_kw)
+    return c, m, s, n, prev_argmax, stable
+
+
 def linear_mask_schedule(length: int, steps: int):
     """Target mask counts m_s = ceil(N (S - s) / S), s = 0..S (Module 12, sec. 6)."""
     if length <= 0 or steps <= 0:

@@ -198,3 +198,25 @@ def confidence(logits):
     arg = np.argmax(logits, axis=1)          # first (lowest) index among equal maxima
     s = np.exp(logits - m[:, None]).sum(axis=1)
     return 1.0 / s, arg.astype(np.int64)
+
+
+def entropy(logits):
+    """Per row: entropy in nats of the softmax of the raw logits, -sum_v p_v ln p_v.
+
+    The EntropyBoundScheduler and adaptive stopping of the DiffusionGemma docs
+    (Schedulers; adaptive stopping) rank and stop on per-token entropy.  The
+    masked-out -inf logit has probability 0 and contributes nothing.  Raises
+    ValueError on other non-finite logits, like ``confidence``.
+    """
+    logits = np.atleast_2d(np.asarray(logits, dtype=F64))
+    if np.isnan(logits).any() or np.isposinf(logits).any():
+        raise ValueError("logits must be finite")
+    if not np.isfinite(logits).any(axis=1).all():
+        raise ValueError("every row needs a finite logit")
+    m = logits.max(axis=1, keepdims=True)
+    e = np.exp(logits - m)                   # exp(-inf) = 0 for the mask id
+    p = e / e.sum(axis=1, keepdims=True)
+    terms = np.zeros_like(p)
+    pos = p > 0
+    terms[pos] = p[pos] * np.log(p[pos])
+    return -terms.sum(axis=1)
