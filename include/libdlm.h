@@ -174,6 +174,19 @@ dlm_status dlm_denoise_step(const dlm_model* m, const dlm_kv* kv, const int32_t*
                             int32_t* argmax, float* logits, int32_t* flags, void* ws, size_t ws_bytes,
                             void* stream);
 
+/* dlm_denoise_step that also writes, at the masked positions, the entropy in
+ * nats of each position's softmax over the vocabulary without the mask id,
+ * -sum_v p_v ln p_v = ln S - sum_v e_v (l_v - max) / S with e_v = exp(l_v - max)
+ * and S = sum_v e_v (the ranking and stopping quantity of the DiffusionGemma
+ * docs' EntropyBoundScheduler and adaptive stopping).  The head accumulates the
+ * second sum beside S in the same pass; no logits are written for it.
+ *   entropy [dev] fp32 [B][L] or NULL (then exactly dlm_denoise_step).
+ * Errors as dlm_denoise_step; INVALID_ARG if entropy is misaligned. */
+dlm_status dlm_denoise_step_ex(const dlm_model* m, const dlm_kv* kv, const int32_t* prefix_len, int32_t max_prefix,
+                               const int32_t* canvas, const uint8_t* masked, int32_t B, int32_t L, float* conf,
+                               int32_t* argmax, float* entropy, float* logits, int32_t* flags, void* ws,
+                               size_t ws_bytes, void* stream);
+
 /* Commit / remask (MLX guide, sec. 5.2 native sampler and sec. 6; DiffusionGemma
  * docs, BlockRefinementScheduler).  Per row b with at least one masked position:
  *   A = { masked j : conf[b][j] > threshold[b] }          (strictly above)
@@ -189,6 +202,52 @@ dlm_status dlm_denoise_step(const dlm_model* m, const dlm_kv* kv, const int32_t*
 dlm_status dlm_commit(const float* conf, const int32_t* argmax, int32_t* canvas, uint8_t* masked, int32_t B,
                       int32_t L, const float* threshold, const int32_t* quota, int32_t* steps, int32_t max_steps,
                       int32_t* n_committed, int32_t* n_left, void* stream);
+
+/* Sampler variants of the commit step. */
+typedef enum {
+  DLM_RULE_THRESHOLD = 0, /* native: conf > threshold (dlm_commit) */
+  DLM_RULE_BOUND = 1,     /* MLX guide, sec. 5.2, confidence_threshold_bound: conf >= threshold, or
+                             conf >= min_threshold and conf >= 1 - scaling / (j + 2), j = position
+                             in the block (float32 arithmetic) */
+  DLM_RULE_ENTROPY = 2    /* DiffusionGemma docs, EntropyBoundScheduler: masked positions in
+                             (entropy, position) order while the float32 running sum of their
+                             entropies stays <= entropy_bound */
+} dlm_commit_rule;
+
+typedef struct {
+  int32_t rule;            /* dlm_commit_rule */
+  float min_threshold;     /* DLM_RULE_BOUND floor (the page's default 0.45) */
+  float scaling;           /* DLM_RULE_BOUND position scaling (the page's default 2.0) */
+  float entropy_bound;     /* DLM_RULE_ENTROPY bound on the summed entropy */
+  int32_t max_transfer;    /* > 0: at most this many positions per step (MLX guide, sec. 5.5,
+                              --max-transfer-per-step); the last allowed step still completes */
+  int32_t stability_steps; /* > 0: adaptive stopping (DiffusionGemma docs): a row whose argmax at
+                              every masked position has not changed for this many consecutive steps
+                              and whose mean masked entropy (float32 sum in position order) is below
+                              stop_entropy commits every remaining mask */
+  float stop_entropy;      /* the page's default 0.005 */
+  int32_t* prev_argmax;    /* [dev] int32 [B][L]: adaptive-stopping state; set to -1 when a block
+                              starts; takes each step's argmax at the masked positions */
+  int32_t* stable;         /* [dev] int32 [B]: consecutive stable steps; 0 when a block starts */
+} dlm_commit_opts;
+
+/* dlm_commit with a sampler rule.  Per row with a masked position: adaptive
+ * stopping first (when enabled); then A as the rule defines it; on the last
+ * allowed step every remaining mask; else A when |A| >= q = min(quota[b],
+ * #masked), otherwise A plus the best-ranked other masked positions up to q;
+ * then the max_transfer cap keeps the best-ranked.  Rank: (-conf, position), or
+ * (entropy, position) for DLM_RULE_ENTROPY.  With DLM_RULE_THRESHOLD and no
+ * cap or stopping this is exactly dlm_commit.
+ *   entropy [dev] fp32 [B][L] (dlm_denoise_step_ex), required by DLM_RULE_ENTROPY
+ *           and by adaptive stopping, else may be NULL
+ *   opts    host struct, read during the call
+ * Errors as dlm_commit; INVALID_ARG for an unknown rule, a non-finite
+ * parameter, max_transfer < 0, stability_steps < 0, or a missing entropy /
+ * state buffer the options need. */
+dlm_status dlm_commit_ex(const float* conf, const int32_t* argmax, const float* entropy, int32_t* canvas,
+                         uint8_t* masked, int32_t B, int32_t L, const float* threshold, const int32_t* quota,
+                         int32_t* steps, int32_t max_steps, const dlm_commit_opts* opts, int32_t* n_committed,
+                         int32_t* n_left, void* stream);
 
 /* Post-block pass (MLX guide, sec. 6; Module 12, sec. 14): a causal pass of the
  * finished block at positions prefix_len[b] + j; its keys/values overwrite cache

@@ -69,13 +69,15 @@ dlm_status dlm_op_attention(const void* q, int32_t ldq, const void* k_cache, con
  * probability over the vocabulary without mask_id and argmax[r] = lowest id
  * reaching the max logit, computed per vocabulary tile and merged, without
  * writing the logits (unless logits [dev] fp32 [R][V] is given; -inf at mask_id).
+ * entropy [dev] fp32 [R] or NULL: the softmax's entropy in nats (as for
+ * dlm_denoise_step_ex).
  * flags [dev] int32 [2] or NULL: flags[0] += rows' tiles with non-finite logits.
  * Requirements: V a multiple of 256; d as K of dlm_op_gemm.
  * ws: dlm_op_lm_head_workspace_bytes(R, V) bytes. */
 size_t dlm_op_lm_head_workspace_bytes(int32_t R, int32_t V);
 dlm_status dlm_op_lm_head(const void* hidden, int32_t R, int32_t d, const void* head, int32_t V, int32_t mask_id,
-                          float* conf, int32_t* argmax, float* logits, int32_t* flags, void* ws, size_t ws_bytes,
-                          void* stream);
+                          float* conf, int32_t* argmax, float* entropy, float* logits, int32_t* flags, void* ws,
+                          size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

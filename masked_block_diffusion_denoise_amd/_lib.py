@@ -21,8 +21,8 @@ TIMER_LM_HEAD, TIMER_ATTENTION, TIMER_GATE_UP, TIMER_DOWN, TIMER_QKV = 0, 1, 2, 
 # Every function declared in include/libdlm.h and include/libdlm_ops.h.
 EXPORTS = [
     "dlm_model_create", "dlm_model_destroy", "dlm_model_set_lora", "dlm_model_enable_lora",
-    "dlm_workspace_bytes", "dlm_prefill", "dlm_denoise_step",
-    "dlm_commit", "dlm_append_block", "dlm_status_string", "dlm_last_error", "dlm_set_kernel_timer",
+    "dlm_workspace_bytes", "dlm_prefill", "dlm_denoise_step", "dlm_denoise_step_ex",
+    "dlm_commit", "dlm_commit_ex", "dlm_append_block", "dlm_status_string", "dlm_last_error", "dlm_set_kernel_timer",
     "dlm_op_gemm_workspace_bytes", "dlm_op_gemm", "dlm_op_rmsnorm", "dlm_op_rope_workspace_bytes",
     "dlm_op_rope_kv", "dlm_op_attention_workspace_bytes", "dlm_op_attention",
     "dlm_op_lm_head_workspace_bytes", "dlm_op_lm_head",
@@ -53,6 +53,16 @@ class KV(C.Structure):
     _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("batch", C.c_int32), ("capacity", C.c_int32)]
 
 
+RULE_THRESHOLD, RULE_BOUND, RULE_ENTROPY = 0, 1, 2
+
+
+class CommitOpts(C.Structure):
+    """dlm_commit_opts: the sampler rule and its parameters (libdlm.h)."""
+    _fields_ = [("rule", C.c_int32), ("min_threshold", C.c_float), ("scaling", C.c_float),
+                ("entropy_bound", C.c_float), ("max_transfer", C.c_int32), ("stability_steps", C.c_int32),
+                ("stop_entropy", C.c_float), ("prev_argmax", C.c_void_p), ("stable", C.c_void_p)]
+
+
 _lib = None
 
 vp, i32, f32, sz = C.c_void_p, C.c_int32, C.c_float, C.c_size_t
@@ -66,6 +76,8 @@ _SIGS = {
     "dlm_prefill": (i32, [vp, C.POINTER(KV), vp, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
     "dlm_denoise_step": (i32, [vp, C.POINTER(KV), vp, i32, vp, vp, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
     "dlm_commit": (i32, [vp, vp, vp, vp, i32, i32, vp, vp, vp, i32, vp, vp, vp]),
+    "dlm_denoise_step_ex": (i32, [vp, C.POINTER(KV), vp, i32, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]),
+    "dlm_commit_ex": (i32, [vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, i32, C.POINTER(CommitOpts), vp, vp, vp]),
     "dlm_append_block": (i32, [vp, C.POINTER(KV), vp, i32, vp, i32, i32, vp, vp, vp, vp, sz, vp]),
     "dlm_status_string": (C.c_char_p, [i32]),
     "dlm_set_kernel_timer": (i32, [i32, vp, vp]),
@@ -79,7 +91,7 @@ _SIGS = {
     "dlm_op_attention": (i32, [vp, i32, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, vp,
                                sz, vp]),
     "dlm_op_lm_head_workspace_bytes": (sz, [i32, i32]),
-    "dlm_op_lm_head": (i32, [vp, i32, i32, vp, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
+    "dlm_op_lm_head": (i32, [vp, i32, i32, vp, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]),
 }
 
 

@@ -332,7 +332,7 @@ dlm_status run_layers(const dlm_model* m, const dlm_kv* kv, const int32_t* token
 // caller already normalised them into p.xn) and the fused head.
 dlm_status run_head(const dlm_model* m, int R, const int* rows, const int* count, const int* out_rows, float* conf,
                     int32_t* argmax, float* logits, int32_t* flags, const PassBufs& p, hipStream_t s,
-                    bool time_head, bool norm = true) {
+                    bool time_head, bool norm = true, float* entropy = nullptr) {
   const dlm_config& c = m->c;
   if (norm) DLM_TRY(rmsnorm(p.x, R, c.d_model, m->final_norm, c.rms_eps, p.xn, rows, count, s), "final norm");
   GemmArgs g{};
@@ -352,7 +352,7 @@ dlm_status run_head(const dlm_model* m, int R, const int* rows, const int* count
     TimerScope t(DLM_TIMER_LM_HEAD, s, time_head);
     DLM_TRY(gemm(g, EPI_HEAD, s), "lm head");
   }
-  DLM_TRY(head_merge(p.head_part, c.vocab / gemm_head_tile_n(R), R, out_rows, count, conf, argmax, R, s),
+  DLM_TRY(head_merge(p.head_part, c.vocab / gemm_head_tile_n(R), R, out_rows, count, conf, argmax, R, s, entropy),
           "head merge");
   return DLM_OK;
 }
@@ -546,11 +546,20 @@ static dlm_status check_block_call(const dlm_model* m, const dlm_kv* kv, const i
 dlm_status dlm_denoise_step(const dlm_model* m, const dlm_kv* kv, const int32_t* prefix_len, int32_t max_prefix,
                             const int32_t* canvas, const uint8_t* masked, int32_t B, int32_t L, float* conf,
                             int32_t* argmax, float* logits, int32_t* flags, void* ws, size_t ws_bytes, void* stream) {
+  return dlm_denoise_step_ex(m, kv, prefix_len, max_prefix, canvas, masked, B, L, conf, argmax, nullptr, logits,
+                             flags, ws, ws_bytes, stream);
+}
+
+dlm_status dlm_denoise_step_ex(const dlm_model* m, const dlm_kv* kv, const int32_t* prefix_len, int32_t max_prefix,
+                               const int32_t* canvas, const uint8_t* masked, int32_t B, int32_t L, float* conf,
+                               int32_t* argmax, float* entropy, float* logits, int32_t* flags, void* ws,
+                               size_t ws_bytes, void* stream) {
   g_err[0] = 0;
   dlm_status st = check_block_call(m, kv, prefix_len, max_prefix, canvas, B, L);
   if (st != DLM_OK) return st;
   if (!masked || !conf || !argmax || !aligned4(conf) || !aligned4(argmax))
     return fail(DLM_ERR_INVALID_ARG, "masked/conf/argmax NULL or misaligned");
+  if (entropy && !aligned4(entropy)) return fail(DLM_ERR_INVALID_ARG, "entropy misaligned");
   if (logits && !aligned16(logits)) return fail(DLM_ERR_INVALID_ARG, "logits must be 16-byte aligned");
   const int R = B * L, max_kv = max_prefix + L;
   const size_t need = carve(m->c, 0, R, B, L, max_kv, false).bytes;
@@ -560,7 +569,7 @@ dlm_status dlm_denoise_step(const dlm_model* m, const dlm_kv* kv, const int32_t*
   if ((st = run_layers(m, kv, canvas, L, B, L, prefix_len, 0, 0, max_kv, flags, p, s)) != DLM_OK) return st;
   DLM_TRY(masked_norm(masked, R, p.x, m->c.d_model, m->final_norm, m->c.rms_eps, p.xn, p.rows, p.count, s),
           "masked rows + final norm");
-  return run_head(m, R, p.rows, p.count, p.rows, conf, argmax, logits, flags, p, s, true, false);
+  return run_head(m, R, p.rows, p.count, p.rows, conf, argmax, logits, flags, p, s, true, false, entropy);
 }
 
 dlm_status dlm_commit(const float* conf, const int32_t* argmax, int32_t* canvas, uint8_t* masked, int32_t B,
@@ -576,6 +585,46 @@ dlm_status dlm_commit(const float* conf, const int32_t* argmax, int32_t* canvas,
   if (!masked) return fail(DLM_ERR_INVALID_ARG, "masked is NULL");
   DLM_TRY(dlm::commit(conf, argmax, canvas, masked, B, L, threshold, quota, steps, max_steps, n_committed, n_left,
                       static_cast<hipStream_t>(stream)),
+          "commit");
+  return DLM_OK;
+}
+
+dlm_status dlm_commit_ex(const float* conf, const int32_t* argmax, const float* entropy, int32_t* canvas,
+                         uint8_t* masked, int32_t B, int32_t L, const float* threshold, const int32_t* quota,
+                         int32_t* steps, int32_t max_steps, const dlm_commit_opts* opts, int32_t* n_committed,
+                         int32_t* n_left, void* stream) {
+  g_err[0] = 0;
+  if (B < 1) return fail(DLM_ERR_SHAPE, "batch %d < 1", B);
+  if (L < 1 || L > 64) return fail(DLM_ERR_SHAPE, "block length %d must be in [1, 64]", L);
+  if (max_steps < 1) return fail(DLM_ERR_INVALID_ARG, "max_steps %d < 1", max_steps);
+  if (!opts) return fail(DLM_ERR_INVALID_ARG, "opts is NULL");
+  const void* ps[] = {conf, argmax, canvas, threshold, quota, steps, n_committed, n_left};
+  for (const void* p : ps)
+    if (!p || !aligned4(p)) return fail(DLM_ERR_INVALID_ARG, "a commit buffer is NULL or misaligned");
+  if (!masked) return fail(DLM_ERR_INVALID_ARG, "masked is NULL");
+  const dlm_commit_opts& o = *opts;
+  if (o.rule < DLM_RULE_THRESHOLD || o.rule > DLM_RULE_ENTROPY) return fail(DLM_ERR_INVALID_ARG, "rule %d", o.rule);
+  if (!std::isfinite(o.min_threshold) || !std::isfinite(o.scaling) || !std::isfinite(o.entropy_bound) ||
+      !std::isfinite(o.stop_entropy))
+    return fail(DLM_ERR_INVALID_ARG, "non-finite sampler parameter");
+  if (o.max_transfer < 0 || o.stability_steps < 0)
+    return fail(DLM_ERR_INVALID_ARG, "max_transfer %d / stability_steps %d < 0", o.max_transfer, o.stability_steps);
+  if ((o.rule == DLM_RULE_ENTROPY || o.stability_steps > 0) && (!entropy || !aligned4(entropy)))
+    return fail(DLM_ERR_INVALID_ARG, "the entropy rule and adaptive stopping need aligned entropies");
+  if (o.stability_steps > 0 && (!o.prev_argmax || !o.stable || !aligned4(o.prev_argmax) || !aligned4(o.stable)))
+    return fail(DLM_ERR_INVALID_ARG, "adaptive stopping needs prev_argmax and stable buffers");
+  CommitOpts co;
+  co.rule = o.rule;
+  co.min_threshold = o.min_threshold;
+  co.scaling = o.scaling;
+  co.entropy_bound = o.entropy_bound;
+  co.max_transfer = o.max_transfer;
+  co.stability_steps = o.stability_steps;
+  co.stop_entropy = o.stop_entropy;
+  co.prev_argmax = o.prev_argmax;
+  co.stable = o.stable;
+  DLM_TRY(dlm::commit(conf, argmax, canvas, masked, B, L, threshold, quota, steps, max_steps, n_committed, n_left,
+                      static_cast<hipStream_t>(stream), entropy, &co),
           "commit");
   return DLM_OK;
 }
@@ -730,13 +779,14 @@ size_t dlm_op_lm_head_workspace_bytes(int32_t R, int32_t V) {
 }
 
 dlm_status dlm_op_lm_head(const void* hidden, int32_t R, int32_t d, const void* head, int32_t V, int32_t mask_id,
-                          float* conf, int32_t* argmax, float* logits, int32_t* flags, void* ws, size_t ws_bytes,
-                          void* stream) {
+                          float* conf, int32_t* argmax, float* entropy, float* logits, int32_t* flags, void* ws,
+                          size_t ws_bytes, void* stream) {
   g_err[0] = 0;
   if (!hidden || !head || !conf || !argmax || !aligned16(hidden) || !aligned16(head) || !aligned4(conf) ||
       !aligned4(argmax))
     return fail(DLM_ERR_INVALID_ARG, "hidden/head/conf/argmax NULL or misaligned");
   if (logits && !aligned16(logits)) return fail(DLM_ERR_INVALID_ARG, "logits must be 16-byte aligned");
+  if (entropy && !aligned4(entropy)) return fail(DLM_ERR_INVALID_ARG, "entropy misaligned");
   if (R < 1 || V < 256 || V % 256 || !gemm_k_ok(d)) return fail(DLM_ERR_SHAPE, "lm head shape R=%d V=%d d=%d", R, V, d);
   if (mask_id < 0 || mask_id >= V) return fail(DLM_ERR_INVALID_ARG, "mask_id %d", mask_id);
   dlm_status st = check_ws(ws, ws_bytes, dlm_op_lm_head_workspace_bytes(R, V));
@@ -754,7 +804,7 @@ dlm_status dlm_op_lm_head(const void* hidden, int32_t R, int32_t d, const void* 
   g.mask_id = mask_id;
   g.nonfinite = flags;
   DLM_TRY(gemm(g, EPI_HEAD, s), "lm head");
-  DLM_TRY(head_merge(ws, V / gemm_head_tile_n(R), R, nullptr, nullptr, conf, argmax, R, s), "head merge");
+  DLM_TRY(head_merge(ws, V / gemm_head_tile_n(R), R, nullptr, nullptr, conf, argmax, R, s, entropy), "head merge");
   return DLM_OK;
 }
 

@@ -71,11 +71,14 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Online-softmax / argmax partial: running max m, sum of exp(l - m), index of the max.
+// Online-softmax / argmax partial: running max m, s = sum of exp(l - m), index
+// of the max, and t = sum of exp(l - m) * (l - m), so that the entropy of the
+// softmax is ln(s) - t / s.
 struct MaxSumIdx {
   float m;
   float s;
   int idx;
+  float t;
 };
 
 // Combine two partials: the max, its lowest index on ties, and the rescaled sum.
@@ -88,9 +91,21 @@ __device__ __forceinline__ MaxSumIdx msi_combine(MaxSumIdx a, MaxSumIdx b) {
     r.m = b.m;
     r.idx = b.idx;
   }
-  float sa = (a.s == 0.f) ? 0.f : a.s * __expf(a.m - r.m);
-  float sb = (b.s == 0.f) ? 0.f : b.s * __expf(b.m - r.m);
+  // rescale each side to the new max: exp(l - M) = exp(m - M) exp(l - m), and
+  // exp(l - M)(l - M) = exp(m - M) [exp(l - m)(l - m) + (m - M) exp(l - m)]
+  float sa = 0.f, ta = 0.f, sb = 0.f, tb = 0.f;
+  if (a.s != 0.f) {
+    const float e = __expf(a.m - r.m);
+    sa = a.s * e;
+    ta = (a.t + (a.m - r.m) * a.s) * e;
+  }
+  if (b.s != 0.f) {
+    const float e = __expf(b.m - r.m);
+    sb = b.s * e;
+    tb = (b.t + (b.m - r.m) * b.s) * e;
+  }
   r.s = sa + sb;
+  r.t = ta + tb;
   return r;
 }
 

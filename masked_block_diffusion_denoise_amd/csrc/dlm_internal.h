@@ -75,9 +75,21 @@ size_t attn_partial_floats_bound(int R, int H, int G, int hd, int max_kv);
 hipError_t attention(const AttnArgs& a, hipStream_t s);
 
 // ------------------------------------------------------------ small ----
+enum CommitRule : int { COMMIT_THRESHOLD = 0, COMMIT_BOUND = 1, COMMIT_ENTROPY = 2 };
+struct CommitOpts {
+  int rule = COMMIT_THRESHOLD;
+  float min_threshold = 0.45f, scaling = 2.f;  // COMMIT_BOUND
+  float entropy_bound = 0.1f;                  // COMMIT_ENTROPY
+  int max_transfer = 0;                        // > 0: at most this many per step (not on the last)
+  int stability_steps = 0;                     // > 0: adaptive stopping
+  float stop_entropy = 0.005f;
+  int* prev_argmax = nullptr;                  // [B][L] adaptive-stopping state
+  int* stable = nullptr;                       // [B]
+};
+// entropy: per-position entropies [B][L] (the entropy rule, adaptive stopping)
 hipError_t commit(const float* conf, const int* argmax, int* canvas, uint8_t* masked, int B, int L,
                   const float* tau, const int* quota, int* steps, int max_steps, int* n_committed,
-                  int* n_left, hipStream_t s);
+                  int* n_left, hipStream_t s, const float* entropy = nullptr, const CommitOpts* opts = nullptr);
 // row m = b*Lq + j takes token tokens[b*tok_ld + j]; with tab, the same launch
 // fills the RoPE table of the pass (rope_table's layout)
 hipError_t embed_norm(const int* tokens, int M, int Lq, int tok_ld, const void* embed, int V, int d,
@@ -100,8 +112,9 @@ hipError_t resid_norm(const float* part, int S, int M, float* x, int d, const vo
 // many, fused with the final RMSNorm of those rows into xn[0..count)
 hipError_t masked_norm(const uint8_t* masked, int M, const float* x, int d, const void* gain, float eps, void* xn,
                        int* rows, int* count, hipStream_t s);
+// entropy (optional): ln(sum exp) - sum exp*(l - max) / sum exp per row, in nats
 hipError_t head_merge(const void* partials, int n_tiles, int M, const int* rows, const int* m_dev,
-                      float* conf, int* argmax, int total_rows, hipStream_t s);
+                      float* conf, int* argmax, int total_rows, hipStream_t s, float* entropy = nullptr);
 hipError_t fill_i32(int* p, int n, int v, hipStream_t s);
 hipError_t fill_f32(float* p, int n, float v, hipStream_t s);
 // prefix[b] = (add ? prefix[b] : 0) + value

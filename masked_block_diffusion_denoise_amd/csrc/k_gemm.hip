@@ -26,7 +26,7 @@ __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)
 // Reduce four logits of columns n0..n0+3 (one row) to a (max, sum exp, argmax) partial.
 __device__ __forceinline__ MaxSumIdx head_quad(const float* v, int n0, int mask_id, bool& bad) {
   float x[4];
-  MaxSumIdx r{-INFINITY, 0.f, 0x7fffffff};
+  MaxSumIdx r{-INFINITY, 0.f, 0x7fffffff, 0.f};
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     x[u] = v[u];
@@ -39,7 +39,12 @@ __device__ __forceinline__ MaxSumIdx head_quad(const float* v, int n0, int mask_
   }
   if (r.m != -INFINITY) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) r.s += __expf(x[u] - r.m);
+    for (int u = 0; u < 4; ++u)
+      if (x[u] != -INFINITY) {  // the mask id adds nothing (0 * -inf would be NaN)
+        const float e = __expf(x[u] - r.m);
+        r.s += e;
+        r.t += e * (x[u] - r.m);
+      }
   }
   return r;
 }
@@ -49,6 +54,7 @@ __device__ __forceinline__ MaxSumIdx msi_shfl_xor(MaxSumIdx a, int mask) {
   b.m = __shfl_xor(a.m, mask, WAVE);
   b.s = __shfl_xor(a.s, mask, WAVE);
   b.idx = __shfl_xor(a.idx, mask, WAVE);
+  b.t = __shfl_xor(a.t, mask, WAVE);
   return msi_combine(a, b);
 }
 
@@ -373,13 +379,19 @@ __global__ void __launch_bounds__(WN * WM * 64) k_gemm_tiled(GemmArgs g) {
         }
       }
   } else if (EPI == EPI_HEAD) {
-    __shared__ float rm[WN * BM], rs[WN * BM];
-    __shared__ int ri[WN * BM];
+    // per (wavefront column, row) partials in the LDS of the ring, free once
+    // every wavefront has left the main loop
+    static_assert(4 * WN * BM * sizeof(float) <= NBUF * STAGE, "head partials must fit in the ring");
+    __syncthreads();
+    float* rm = reinterpret_cast<float*>(lds);
+    float* rs = rm + WN * BM;
+    float* rt = rs + WN * BM;
+    int* ri = reinterpret_cast<int*>(rt + WN * BM);
     bool bad = false;
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
       const int ml = (wm * TM + j) * 32 + arow, m = m0 + ml;
-      MaxSumIdx p{-INFINITY, 0.f, 0x7fffffff};
+      MaxSumIdx p{-INFINITY, 0.f, 0x7fffffff, 0.f};
 #pragma unroll
       for (int i = 0; i < TN; ++i)
 #pragma unroll
@@ -397,6 +409,7 @@ __global__ void __launch_bounds__(WN * WM * 64) k_gemm_tiled(GemmArgs g) {
       if (ahalf == 0) {
         rm[wn * BM + ml] = p.m;
         rs[wn * BM + ml] = p.s;
+        rt[wn * BM + ml] = p.t;
         ri[wn * BM + ml] = p.idx;
       }
     }
@@ -404,12 +417,13 @@ __global__ void __launch_bounds__(WN * WM * 64) k_gemm_tiled(GemmArgs g) {
     __syncthreads();
     for (int ml = threadIdx.x; ml < BM; ml += T) {
       const int m = m0 + ml;
-      MaxSumIdx p{rm[ml], rs[ml], ri[ml]};
+      MaxSumIdx p{rm[ml], rs[ml], ri[ml], rt[ml]};
 #pragma unroll
-      for (int q = 1; q < WN; ++q) p = msi_combine(p, MaxSumIdx{rm[q * BM + ml], rs[q * BM + ml], ri[q * BM + ml]});
+      for (int q = 1; q < WN; ++q)
+        p = msi_combine(p, MaxSumIdx{rm[q * BM + ml], rs[q * BM + ml], ri[q * BM + ml], rt[q * BM + ml]});
       if (m < M)
         reinterpret_cast<float4*>(g.partials)[static_cast<size_t>(n0 / BN) * g.M + m] =
-            make_float4(p.m, p.s, __int_as_float(p.idx), 0.f);
+            make_float4(p.m, p.s, __int_as_float(p.idx), p.t);
     }
   }
 }

@@ -7,19 +7,40 @@
 namespace dlm {
 
 // ------------------------------------------------------------ commit ----
-// Commit rule (MLX-VLM Nemotron Labs Diffusion guide, sec. 5.2 native sampler and
-// sec. 6; DiffusionGemma docs, BlockRefinementScheduler): per row, A = masked
-// positions with conf > tau; q = #masked on the last allowed step, else
-// min(quota, #masked); the top max(|A|, q) masked positions by (-conf, position)
-// take their argmax token and leave the mask; the others stay masked.  Rows with
-// no mask left are frozen.  One wavefront per row (L <= 64).
+// Commit rules, one wavefront per row (L <= 64), lane j = position j.
+//
+// Native (MLX-VLM Nemotron Labs Diffusion guide, sec. 5.2 native sampler and
+// sec. 6; DiffusionGemma docs, BlockRefinementScheduler): A = masked positions
+// with conf > tau.  Bounded (the guide's confidence_threshold_bound, sec. 5.2):
+// conf >= tau, or conf >= min_threshold and conf >= 1 - scaling / (j + 2).
+// Entropy bound (DiffusionGemma docs, EntropyBoundScheduler): masked positions
+// in (entropy, position) order while the float32 running sum of their entropies
+// stays <= the bound.  Then: on the last allowed step every remaining mask;
+// otherwise A when |A| >= q = min(quota, #masked), else A plus the best-ranked
+// others up to q; with max_transfer > 0 (the guide's --max-transfer-per-step,
+// sec. 5.5) at most that many, the best-ranked.  Rank: (-conf, position), or
+// (entropy, position) for the entropy rule.  Chosen positions take their argmax
+// token and leave the mask; the others stay masked.
+//
+// Adaptive stopping (DiffusionGemma docs, adaptive stopping), before the rule:
+// stable[b] counts consecutive steps whose argmax at every masked position
+// equals prev_argmax; when it reaches stability_steps and the mean entropy of
+// the masked positions (float32 sum in position order) is below stop_entropy,
+// every remaining mask is committed.  prev_argmax takes this step's argmax.
+// Rows with no mask left are frozen (no state changes).
+__device__ __forceinline__ bool commit_better(bool by_entropy, float ci, float ei, int i, float cj, float ej, int j) {
+  if (by_entropy) return ei < ej || (ei == ej && i < j);
+  return ci > cj || (ci == cj && i < j);
+}
+
 __global__ void __launch_bounds__(256) k_commit(const float* __restrict__ conf,
                                                 const int* __restrict__ argmax, int* __restrict__ canvas,
                                                 uint8_t* __restrict__ masked, int B, int L,
                                                 const float* __restrict__ tau,
                                                 const int* __restrict__ quota, int* __restrict__ steps,
                                                 int max_steps, int* __restrict__ n_committed,
-                                                int* __restrict__ n_left) {
+                                                int* __restrict__ n_left, const float* __restrict__ entropy,
+                                                CommitOpts o) {
   const int lane = threadIdx.x & 63;
   const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (b >= B) return;  // uniform per wavefront
@@ -27,6 +48,7 @@ __global__ void __launch_bounds__(256) k_commit(const float* __restrict__ conf,
   const bool in = lane < L;
   const bool mk = in && masked[base + lane] != 0;
   const float c = in ? conf[base + lane] : 0.f;
+  const float e = (in && entropy) ? entropy[base + lane] : 0.f;
   const unsigned long long mball = __ballot(mk);
   const int cnt = __popcll(mball);
   if (cnt == 0) {
@@ -37,18 +59,81 @@ __global__ void __launch_bounds__(256) k_commit(const float* __restrict__ conf,
     return;
   }
   const int st = steps[b];
-  const float t = tau[b];
-  const int above = __popcll(__ballot(mk && c > t));
-  const int q = (st >= max_steps - 1) ? cnt : min(quota[b], cnt);
-  const int n = max(above, q);
+  const int a = in ? argmax[base + lane] : 0;
+
+  bool stop = false;
+  if (o.stability_steps > 0) {
+    const bool diff = mk && a != o.prev_argmax[base + lane];
+    const int stable = __any(diff) ? 0 : o.stable[b] + 1;
+    float total = 0.f;  // sequential, in position order
+    for (int i = 0; i < L; ++i) {
+      const float ei = __shfl(e, i, WAVE);
+      if ((mball >> i) & 1ull) total = total + ei;
+    }
+    const float mean = total / static_cast<float>(cnt);
+    stop = stable >= o.stability_steps && mean < o.stop_entropy;
+    if (mk) o.prev_argmax[base + lane] = a;
+    if (lane == 0) o.stable[b] = stable;
+  }
+
+  const bool by_ent = o.rule == COMMIT_ENTROPY;
+  // rank among the masked positions by the rule's order
   int rank = 0;
   for (int i = 0; i < L; ++i) {
-    const float ci = __shfl(c, i, WAVE);
+    const float ci = __shfl(c, i, WAVE), ei = __shfl(e, i, WAVE);
     const bool mi = (mball >> i) & 1ull;
-    rank += (mi && (ci > c || (ci == c && i < lane))) ? 1 : 0;
+    rank += (mi && commit_better(by_ent, ci, ei, i, c, e, lane)) ? 1 : 0;
   }
-  if (mk && rank < n) {
-    canvas[base + lane] = argmax[base + lane];
+  bool chosen;
+  int n;
+  if (stop || st >= max_steps - 1) {
+    chosen = mk;
+    n = cnt;
+  } else {
+    bool inA;
+    if (o.rule == COMMIT_BOUND) {
+      inA = mk && (c >= tau[b] || (c >= o.min_threshold && c >= 1.f - o.scaling / static_cast<float>(lane + 2)));
+    } else if (o.rule == COMMIT_ENTROPY) {
+      // running sum of the entropies in rank order (float32, sequential)
+      float total = 0.f, mine = 0.f;
+      for (int r = 0; r < cnt; ++r) {
+        const int src = __ffsll(static_cast<long long>(__ballot(mk && rank == r))) - 1;
+        total = total + __shfl(e, src, WAVE);
+        if (rank == r) mine = total;
+      }
+      inA = mk && mine <= o.entropy_bound;
+    } else {
+      inA = mk && c > tau[b];
+    }
+    const unsigned long long aball = __ballot(inA);
+    const int nA = __popcll(aball);
+    const int q = min(quota[b], cnt);
+    if (nA >= q) {
+      chosen = inA;
+      n = nA;
+    } else {  // A plus the best-ranked others up to q
+      int orank = 0;
+      for (int i = 0; i < L; ++i) {
+        const float ci = __shfl(c, i, WAVE), ei = __shfl(e, i, WAVE);
+        const bool oi = ((mball & ~aball) >> i) & 1ull;
+        orank += (oi && commit_better(by_ent, ci, ei, i, c, e, lane)) ? 1 : 0;
+      }
+      chosen = inA || (mk && orank < q - nA);
+      n = q;
+    }
+    if (o.max_transfer > 0 && n > o.max_transfer) {
+      const unsigned long long cball = __ballot(chosen);
+      int crank = 0;
+      for (int i = 0; i < L; ++i) {
+        const float ci = __shfl(c, i, WAVE), ei = __shfl(e, i, WAVE);
+        crank += (((cball >> i) & 1ull) && commit_better(by_ent, ci, ei, i, c, e, lane)) ? 1 : 0;
+      }
+      chosen = chosen && crank < o.max_transfer;
+      n = o.max_transfer;
+    }
+  }
+  if (chosen) {
+    canvas[base + lane] = a;
     masked[base + lane] = 0;
   }
   if (lane == 0) {
@@ -60,9 +145,10 @@ __global__ void __launch_bounds__(256) k_commit(const float* __restrict__ conf,
 
 hipError_t commit(const float* conf, const int* argmax, int* canvas, uint8_t* masked, int B, int L,
                   const float* tau, const int* quota, int* steps, int max_steps, int* n_committed,
-                  int* n_left, hipStream_t s) {
+                  int* n_left, hipStream_t s, const float* entropy, const CommitOpts* opts) {
+  const CommitOpts o = opts ? *opts : CommitOpts{};
   hipLaunchKernelGGL(k_commit, dim3((B + 3) / 4), dim3(256), 0, s, conf, argmax, canvas, masked, B, L,
-                     tau, quota, steps, max_steps, n_committed, n_left);
+                     tau, quota, steps, max_steps, n_committed, n_left, entropy, o);
   return hipGetLastError();
 }
 
@@ -406,33 +492,36 @@ hipError_t masked_norm(const uint8_t* masked, int M, const float* x, int d, cons
 }
 
 // --------------------------------------------------------- head merge ----
-// Per scored row: merge the per-vocab-tile (max, sum exp, argmax) partials in a
-// fixed order, then conf = 1 / sum_v exp(l_v - max) and the argmax (lowest id on
-// ties) go to position rows[i] of the canvas.
+// Per scored row: merge the per-vocab-tile (max, sum exp, argmax, sum exp*(l -
+// max)) partials in a fixed order, then conf = 1 / sum_v exp(l_v - max), the
+// argmax (lowest id on ties) and optionally the entropy ln(s) - t / s go to
+// position rows[i] of the canvas.
 __global__ void __launch_bounds__(256) k_head_merge(const float4* __restrict__ part, int n_tiles, int M,
                                                     const int* __restrict__ rows,
                                                     const int* __restrict__ m_dev, float* __restrict__ conf,
-                                                    int* __restrict__ argmax) {
-  __shared__ float sm[256], ss[256];
+                                                    int* __restrict__ argmax, float* __restrict__ entropy) {
+  __shared__ float sm[256], ss[256], st[256];
   __shared__ int si[256];
   const int i = blockIdx.x;
   if (m_dev && i >= *m_dev) return;
-  MaxSumIdx acc{-INFINITY, 0.f, 0x7fffffff};
+  MaxSumIdx acc{-INFINITY, 0.f, 0x7fffffff, 0.f};
   for (int t = threadIdx.x; t < n_tiles; t += 256) {
     const float4 p = part[static_cast<size_t>(t) * M + i];
-    acc = msi_combine(acc, MaxSumIdx{p.x, p.y, __float_as_int(p.z)});
+    acc = msi_combine(acc, MaxSumIdx{p.x, p.y, __float_as_int(p.z), p.w});
   }
   sm[threadIdx.x] = acc.m;
   ss[threadIdx.x] = acc.s;
+  st[threadIdx.x] = acc.t;
   si[threadIdx.x] = acc.idx;
   __syncthreads();
   for (int w = 128; w > 0; w >>= 1) {
     if (threadIdx.x < w) {
-      MaxSumIdx a{sm[threadIdx.x], ss[threadIdx.x], si[threadIdx.x]};
-      MaxSumIdx c{sm[threadIdx.x + w], ss[threadIdx.x + w], si[threadIdx.x + w]};
+      MaxSumIdx a{sm[threadIdx.x], ss[threadIdx.x], si[threadIdx.x], st[threadIdx.x]};
+      MaxSumIdx c{sm[threadIdx.x + w], ss[threadIdx.x + w], si[threadIdx.x + w], st[threadIdx.x + w]};
       a = msi_combine(a, c);
       sm[threadIdx.x] = a.m;
       ss[threadIdx.x] = a.s;
+      st[threadIdx.x] = a.t;
       si[threadIdx.x] = a.idx;
     }
     __syncthreads();
@@ -441,14 +530,15 @@ __global__ void __launch_bounds__(256) k_head_merge(const float4* __restrict__ p
     const int dst = rows ? rows[i] : i;
     conf[dst] = 1.0f / ss[0];
     argmax[dst] = si[0];
+    if (entropy) entropy[dst] = logf(ss[0]) - st[0] / ss[0];
   }
 }
 
 hipError_t head_merge(const void* partials, int n_tiles, int M, const int* rows, const int* m_dev,
-                      float* conf, int* argmax, int total_rows, hipStream_t s) {
+                      float* conf, int* argmax, int total_rows, hipStream_t s, float* entropy) {
   if (total_rows <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_head_merge, dim3(total_rows), dim3(256), 0, s, static_cast<const float4*>(partials),
-                     n_tiles, M, rows, m_dev, conf, argmax);
+                     n_tiles, M, rows, m_dev, conf, argmax, entropy);
   return hipGetLastError();
 }
 

@@ -204,6 +204,43 @@ class KVCache:
 
 
 @dataclass
+class Sampler:
+    """Commit rule and parameters of dlm_commit_ex (MLX guide, sec. 5.2 and 5.5;
+    DiffusionGemma docs, Schedulers and adaptive stopping).
+
+    rule: "threshold" (native), "bound" (confidence_threshold_bound) or
+    "entropy" (entropy bound).  stability_steps > 0 enables adaptive stopping.
+    """
+    rule: str = "threshold"
+    min_threshold: float = 0.45
+    scaling: float = 2.0
+    entropy_bound: float = 0.1
+    max_transfer: int = 0
+    stability_steps: int = 0
+    stop_entropy: float = 0.005
+
+    RULES = {"threshold": L.RULE_THRESHOLD, "bound": L.RULE_BOUND, "entropy": L.RULE_ENTROPY}
+
+    @property
+    def needs_entropy(self) -> bool:
+        return self.rule == "entropy" or self.stability_steps > 0
+
+    def opts(self, sess: "Session") -> L.CommitOpts:
+        if self.rule not in self.RULES:
+            raise ValueError(f"unknown rule {self.rule!r}")
+        if self.stability_steps > 0 and sess.prev_argmax is None:
+            dev = sess.m.device
+            sess.prev_argmax = torch.full((sess.B, sess.Lb), -1, dtype=torch.int32, device=dev)
+            sess.stable = torch.zeros(sess.B, dtype=torch.int32, device=dev)
+        stab = self.stability_steps > 0
+        return L.CommitOpts(rule=self.RULES[self.rule], min_threshold=self.min_threshold, scaling=self.scaling,
+                            entropy_bound=self.entropy_bound, max_transfer=self.max_transfer,
+                            stability_steps=self.stability_steps, stop_entropy=self.stop_entropy,
+                            prev_argmax=sess.prev_argmax.data_ptr() if stab else None,
+                            stable=sess.stable.data_ptr() if stab else None)
+
+
+@dataclass
 class Stats:
     """Counters of the MLX guide, sec. 9: denoise and post-block forwards, tokens per forward."""
     denoise_nfe: int = 0
@@ -235,6 +272,7 @@ class Session:
         self.flags = torch.zeros(2, dtype=torch.int32, device=dev)
         self.ws = Workspace(dev)
         self.max_prefix = 0
+        self.prev_argmax = self.stable = None  # allocated by a sampler with adaptive stopping
 
     # --- the four calls of the ABI, on the current stream ---------------------
     def prefill(self, tokens: torch.Tensor, ws_rows: int | None = None, last_argmax: torch.Tensor | None = None,
@@ -277,16 +315,26 @@ class Session:
                _p(tokens), B, Lb, _p(argmax_out), _p(conf_out), _p(self.flags), ws, n, stream_handle())
         self.max_prefix += Lb
 
-    def denoise_step(self, logits: torch.Tensor | None = None):
+    def denoise_step(self, logits: torch.Tensor | None = None, entropy: torch.Tensor | None = None):
+        """dlm_denoise_step on the session canvas; with ``entropy`` (fp32 [B, L])
+        dlm_denoise_step_ex also writes each masked position's entropy."""
         B, Lb = self.B, self.Lb
         ws, n = self.ws.get(self.m.workspace_bytes(B * Lb, self.max_prefix + Lb))
-        L.call("dlm_denoise_step", self.m.handle, C.byref(self.kv.c), _p(self.prefix), self.max_prefix,
-               _p(self.canvas), _p(self.masked), B, Lb, _p(self.conf), _p(self.argmax), _p(logits),
+        L.call("dlm_denoise_step_ex", self.m.handle, C.byref(self.kv.c), _p(self.prefix), self.max_prefix,
+               _p(self.canvas), _p(self.masked), B, Lb, _p(self.conf), _p(self.argmax), _p(entropy), _p(logits),
                _p(self.flags), ws, n, stream_handle())
 
     def commit(self, tau: torch.Tensor, quota: torch.Tensor, max_steps: int):
         L.call("dlm_commit", _p(self.conf), _p(self.argmax), _p(self.canvas), _p(self.masked), self.B,
                self.Lb, _p(tau), _p(quota), _p(self.steps), max_steps, _p(self.n_committed),
+               _p(self.n_left), stream_handle())
+
+    def commit_ex(self, tau: torch.Tensor, quota: torch.Tensor, max_steps: int, sampler: "Sampler",
+                  entropy: torch.Tensor | None = None):
+        """dlm_commit_ex with a sampler rule (see Sampler)."""
+        o = sampler.opts(self)
+        L.call("dlm_commit_ex", _p(self.conf), _p(self.argmax), _p(entropy), _p(self.canvas), _p(self.masked),
+               self.B, self.Lb, _p(tau), _p(quota), _p(self.steps), max_steps, C.byref(o), _p(self.n_committed),
                _p(self.n_left), stream_handle())
 
     def append_block(self, argmax_out=None, conf_out=None):
@@ -301,18 +349,27 @@ class Session:
         self.canvas.fill_(self.m.cfg.mask_id)
         self.masked.fill_(1)
         self.steps.zero_()
+        if self.prev_argmax is not None:  # adaptive-stopping state
+            self.prev_argmax.fill_(-1)
+            self.stable.zero_()
 
     # --- driver loop ----------------------------------------------------------
     def generate(self, prompt: torch.Tensor, gen_length: int, max_steps: int, threshold: float = 0.9,
-                 quota: int = 1):
+                 quota: int = 1, sampler: "Sampler | None" = None):
         """Prefill, then blocks of denoise+commit until no mask is left, then append.
 
         Rows advance block by block in lockstep; a finished row is frozen until
-        every row of the batch has finished its block.  Returns (tokens [B, G], stats).
+        every row of the batch has finished its block.  ``sampler`` selects a
+        commit rule other than the native threshold rule.  Returns (tokens [B, G], stats).
         """
         dev = self.m.device
         tau = torch.full((self.B,), threshold, dtype=torch.float32, device=dev)
         q = torch.full((self.B,), quota, dtype=torch.int32, device=dev)
+        ent = None
+        if sampler is not None and sampler.needs_entropy:
+            ent = torch.zeros(self.B, self.Lb, dtype=torch.float32, device=dev)
+        if sampler is not None:
+            sampler.opts(self)  # allocates the adaptive-stopping state before the first block
         self.prefill(prompt)
         out = []
         st = Stats()
@@ -321,8 +378,11 @@ class Session:
             self.begin_block()
             steps = 0
             while True:
-                self.denoise_step()
-                self.commit(tau, q, max_steps)
+                self.denoise_step(entropy=ent)
+                if sampler is None:
+                    self.commit(tau, q, max_steps)
+                else:
+                    self.commit_ex(tau, q, max_steps, sampler, ent)
                 steps += 1
                 st.denoise_nfe += 1
                 st.accepted_tokens += int(self.n_committed.sum().item())

@@ -23,7 +23,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-from .model import KVCache, forward, head_logits, confidence
+from .model import KVCache, forward, head_logits, confidence, entropy
 
 
 def commit(conf, argmax, canvas, masked, tau, quota, step, max_steps):
@@ -263,11 +263,15 @@ class BlockStats:
 
 
 def generate_block_diffusion(w, shape, prompt, gen_length, block_length, max_steps,
-                             tau=0.9, quota=1, keep_trace=False):
+                             tau=0.9, quota=1, keep_trace=False, sampler=None):
     """Block-diffusion decoding of one sequence; returns (generated tokens, stats, cache).
 
     All block positions start as the mask id (no anchor token).  A generation
-    length that is not a multiple of the block length is rounded up.
+    length that is not a multiple of the block length is rounded up.  With
+    ``sampler`` (keyword arguments of ``commit_ex``: rule, min_threshold,
+    scaling, entropy_bound, max_transfer, stability_steps, stop_entropy) the
+    step uses that commit rule; confidences and entropies are rounded to float32
+    first, as the device computes them.
     """
     cache, _ = prefill(w, shape, prompt)
     n_blocks = -(-gen_length // block_length)
@@ -277,12 +281,19 @@ def generate_block_diffusion(w, shape, prompt, gen_length, block_length, max_ste
         canvas = np.full(block_length, shape.mask_id, dtype=np.int64)
         masked = np.ones(block_length, dtype=bool)
         step = 0
+        prev, stable = np.full(block_length, -1), 0
         while masked.any():
             logits = denoise_logits(w, shape, cache, canvas)
             st.masked_rows_scored += int(masked.sum())
             conf, arg = confidence(logits)
-            canvas, masked_new, step, n = commit(conf, arg, canvas, masked, tau, quota,
-                                                 step, max_steps)
+            if sampler is None:
+                canvas, masked_new, step, n = commit(conf, arg, canvas, masked, tau, quota,
+                                                     step, max_steps)
+            else:
+                ent = entropy(logits).astype(np.float32)
+                canvas, masked_new, step, n, prev, stable = commit_ex(
+                    conf.astype(np.float32), arg, canvas, masked, tau, quota, step, max_steps, entropy=ent,
+                    prev_argmax=prev, stable=stable, **sampler)
             if keep_trace:
                 st.trace.append((tuple(np.flatnonzero(masked & ~masked_new).tolist()),
                                  canvas.copy()))

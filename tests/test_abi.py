@@ -135,6 +135,41 @@ def test_commit_validation():
     assert run(masked=None) == -1
 
 
+def test_commit_ex_validation():
+    lib = L.load()
+    f = FAKE
+
+    def run(rule=L.RULE_THRESHOLD, entropy=None, B=2, Lb=8, max_steps=4, opts=True, **kw):
+        o = L.CommitOpts(rule=rule, min_threshold=0.45, scaling=2.0, entropy_bound=0.1, max_transfer=0,
+                         stability_steps=0, stop_entropy=0.005, prev_argmax=None, stable=None)
+        for k, v in kw.items():
+            setattr(o, k, v)
+        return lib.dlm_commit_ex(f, f, entropy, f, f, B, Lb, f, f, f, max_steps, C.byref(o) if opts else None,
+                                 f, f, None)
+    assert run(B=0) == -2
+    assert run(Lb=65) == -2
+    assert run(max_steps=0) == -1
+    assert run(opts=False) == -1
+    assert run(rule=3) == -1
+    assert run(rule=-1) == -1
+    assert run(rule=L.RULE_ENTROPY) == -1                 # the entropy rule needs entropies
+    assert run(min_threshold=float("nan")) == -1
+    assert run(scaling=float("inf")) == -1
+    assert run(max_transfer=-1) == -1
+    assert run(stability_steps=-2) == -1
+    assert run(stability_steps=2, entropy=f) == -1        # stopping needs its state buffers
+    assert run(stability_steps=2) == -1                   # ... and entropies
+    assert b"adaptive" in lib.dlm_last_error() or b"entrop" in lib.dlm_last_error()
+
+
+def test_denoise_step_ex_validation(model):
+    lib = L.load()
+    kv = L.KV(4096, 4096, 1, 64)
+    # a misaligned entropy buffer is refused before anything runs
+    assert lib.dlm_denoise_step_ex(model, C.byref(kv), FAKE, 0, FAKE, FAKE, 1, 16, FAKE, FAKE, C.c_void_p(4098),
+                                   None, None, FAKE, 1 << 30, None) == -1
+
+
 def test_prefill_and_append_validation(model):
     lib = L.load()
     kv = L.KV(4096, 4096, 1, 64)
@@ -154,10 +189,13 @@ def test_op_validation():
     assert lib.dlm_op_gemm(FAKE, FAKE, FAKE, 32, 128, 300, 300, 128, 0, FAKE, 1 << 30, None) == -2
     assert lib.dlm_op_gemm(FAKE, FAKE, FAKE, 32, 128, 128, 128, 128, 3, FAKE, 1 << 30, None) == -1
     assert lib.dlm_op_gemm(FAKE, FAKE, FAKE, 32, 128, 128, 64, 128, 0, FAKE, 1 << 30, None) == -2
-    assert lib.dlm_op_lm_head(FAKE, 4, 128, FAKE, 1024, 1024, FAKE, FAKE, None, None, FAKE, 1 << 30,
+    assert lib.dlm_op_lm_head(FAKE, 4, 128, FAKE, 1024, 1024, FAKE, FAKE, None, None, None, FAKE, 1 << 30,
                               None) == -1
     # the head's vocabulary tiles are 256 wide
-    assert lib.dlm_op_lm_head(FAKE, 4, 128, FAKE, 1152, 0, FAKE, FAKE, None, None, FAKE, 1 << 30, None) == -2
+    assert lib.dlm_op_lm_head(FAKE, 4, 128, FAKE, 1152, 0, FAKE, FAKE, None, None, None, FAKE, 1 << 30,
+                              None) == -2
+    assert lib.dlm_op_lm_head(FAKE, 4, 128, FAKE, 1024, 0, FAKE, FAKE, C.c_void_p(4098), None, None, FAKE,
+                              1 << 30, None) == -1  # misaligned entropy
     assert lib.dlm_op_attention(FAKE, 128, FAKE, FAKE, FAKE, None, 0, 1, 16, 4, 2, 64, 64, 0, 16, FAKE,
                                 1 << 30, None) == -4
     assert lib.dlm_op_attention(FAKE, 128, FAKE, FAKE, FAKE, None, 0, 1, 16, 4, 2, 32, 64, 0, 65, FAKE,

@@ -29,16 +29,20 @@ def check(R, V, d, mask_id, seed, planted=True, with_logits=True):
     th, tw = bf16(h), bf16(w)
     conf = torch.zeros(R, dtype=torch.float32, device="cuda")
     arg = torch.zeros(R, dtype=torch.int32, device="cuda")
+    ent = torch.zeros(R, dtype=torch.float32, device="cuda")
     logits = torch.zeros(R, V, dtype=torch.float32, device="cuda") if with_logits else None
     flags = i32(np.zeros(2))
     ws, n = workspace(L.load().dlm_op_lm_head_workspace_bytes(R, V))
-    L.call("dlm_op_lm_head", p(th), R, d, p(tw), V, mask_id, p(conf), p(arg), p(logits), p(flags), ws, n,
+    L.call("dlm_op_lm_head", p(th), R, d, p(tw), V, mask_id, p(conf), p(arg), p(ent), p(logits), p(flags), ws, n,
            stream())
     sync()
     lg = oracle_logits(h, w, mask_id)
     c_want, a_want = oracle.confidence(lg)
     c_got, a_got = host(conf), host(arg)
     assert np.abs(c_got - c_want).max() < 1e-2
+    # entropy: fp32 logits of the same bf16 products (summation order only) and
+    # fp32 accumulation of the two sums over V; 1e-3 nats covers both at V <= 131072
+    assert np.abs(host(ent) - oracle.entropy(lg)).max() < 1e-3
     top2 = np.sort(lg, axis=1)[:, -2:]
     margin = top2[:, 1] - top2[:, 0]
     sure = margin > 5e-2
@@ -93,6 +97,6 @@ def test_lm_head_flags_non_finite():
     arg = torch.zeros(R, dtype=torch.int32, device="cuda")
     flags = i32(np.zeros(2))
     ws, n = workspace(L.load().dlm_op_lm_head_workspace_bytes(R, V))
-    L.call("dlm_op_lm_head", p(th), R, d, p(tw), V, 0, p(conf), p(arg), None, p(flags), ws, n, stream())
+    L.call("dlm_op_lm_head", p(th), R, d, p(tw), V, 0, p(conf), p(arg), None, None, p(flags), ws, n, stream())
     sync()
     assert host(flags)[0] > 0

@@ -304,3 +304,105 @@ def test_two_wide_layers_split_reductions_prefill_denoise_append():
         if top2[1] - top2[0] > 5e-2:
             assert host(arg)[0, j] == arg_o[j], j
     assert (host(sess.flags) == 0).all()
+
+
+def check_step_first_order(conf_g, arg_g, logits_g, logits_o, masked):
+    """check_step for a large head gain, which scales the logits and so their
+    absolute error: logits within 2e-2 relative RMS as always; the argmax equal
+    wherever the top-1 margin exceeds both 5e-2 and twice the row's largest
+    logit error (below that, the error alone can reorder the two); the
+    confidence within its first-order change under the measured logit error,
+    d ln p_max / d l_k = [k = top] - p_k, so |d conf| ~ conf |d_top - sum_k p_k d_k|
+    (twice that plus 1e-3)."""
+    conf_o, arg_o = oracle.confidence(logits_o)
+    fin = np.isfinite(logits_o[0])
+    for j in np.flatnonzero(masked):
+        l, g = logits_o[j][fin], logits_g[j][fin]
+        assert rel_rms(g, l) < 2e-2
+        d = g - l
+        top2 = np.sort(l)[-2:]
+        if top2[1] - top2[0] > max(5e-2, 2.0 * np.abs(d).max()):
+            assert arg_g[j] == arg_o[j]
+        pr = np.exp(l - l.max())
+        pr /= pr.sum()
+        bar = 2.0 * conf_o[j] * abs(d[np.argmax(l)] - np.sum(pr * d)) + 1e-3
+        assert abs(conf_g[j] - conf_o[j]) <= bar, (j, conf_g[j], conf_o[j], bar)
+    return conf_o, arg_o
+
+
+def entropy_bar(lg_g, lo):
+    """First-order bound on the entropy error from the logit error of each row:
+    dH/dl_k = -p_k (l_k - mean_p l), so |dH| ~ |sum_k p_k (l_k - lbar) d_k|;
+    twice that plus 1e-3 nats covers the second order and fp32 rounding."""
+    fin = np.isfinite(lo)
+    out = np.empty(len(lo))
+    for j in range(len(lo)):
+        l, d = lo[j][fin[j]], (lg_g[j][fin[j]] - lo[j][fin[j]])
+        p = np.exp(l - l.max())
+        p /= p.sum()
+        out[j] = 2.0 * abs(np.sum(p * (l - np.sum(p * l)) * d)) + 1e-3
+    return out
+
+
+@pytest.mark.parametrize("sampler", [dict(rule="entropy", entropy_bound=0.5), dict(rule="bound"),
+                                     dict(rule="threshold", max_transfer=2),
+                                     dict(rule="threshold", stability_steps=2, stop_entropy=0.5)],
+                         ids=["entropy", "bound", "cap2", "adaptive-stop"])
+def test_tiny_teacher_forced_samplers(sampler):
+    """Sampler variants through whole blocks: the device's entropies against the
+    oracle's, and dlm_commit_ex fed the oracle's confidences and entropies
+    bit-exact with the oracle's commit_ex (adaptive-stopping state included)."""
+    announce(f"tiny teacher-forced sampler {sampler}")
+    w = synth.model_weights(TINY, seed=0, lm_head_gain=60.0)
+    m = make(TINY, w)
+    prompt = synth.prompt(TINY, 1, 32, seed=0)
+    Lb, max_steps, tau = 16, 16, 0.9
+    sess = R.Session(m, 1, 128, Lb)
+    sess.prefill(i32(prompt))
+    cache, _ = oracle.prefill(w, TINY, prompt[0])
+    logits = torch.zeros(Lb, TINY.vocab, dtype=torch.float32, device="cuda")
+    ent_g = torch.zeros(1, Lb, dtype=torch.float32, device="cuda")
+    smp = R.Sampler(**sampler)
+    tau_t, q_t = f32([tau]), i32([1])
+    steps_seen = []
+    for blk in range(2):
+        sess.begin_block()
+        canvas = np.full(Lb, TINY.mask_id, np.int64)
+        masked = np.ones(Lb, bool)
+        step, prev, stable = 0, np.full(Lb, -1), 0
+        while masked.any():
+            lo = oracle.denoise_logits(w, TINY, cache, canvas)
+            sess.canvas.copy_(i32(canvas[None]))
+            sess.masked.copy_(u8(masked[None]))
+            sess.denoise_step(logits, ent_g)
+            sync()
+            lg = host(logits)
+            conf_o, arg_o = check_step_first_order(host(sess.conf)[0], host(sess.argmax)[0], lg, lo, masked)
+            ent_o = oracle.entropy(lo)
+            mk = np.flatnonzero(masked)
+            bar = entropy_bar(lg[mk], lo[mk])
+            assert (np.abs(host(ent_g)[0][mk] - ent_o[mk]) <= bar).all(), (host(ent_g)[0][mk], ent_o[mk], bar)
+            # commit on the device fed with the oracle's values: bit-exact
+            c32, e32 = conf_o.astype(np.float32), ent_o.astype(np.float32)
+            sess.conf.copy_(f32(c32[None]))
+            sess.argmax.copy_(i32(arg_o[None]))
+            ent_g.copy_(f32(e32[None]))
+            sess.steps.fill_(step)
+            sess.commit_ex(tau_t, q_t, max_steps, smp, ent_g)
+            canvas, masked, step, n, prev, stable = oracle.commit_ex(
+                c32, arg_o, canvas, masked, tau, 1, step, max_steps, entropy=e32, prev_argmax=prev,
+                stable=stable, **sampler)
+            sync()
+            np.testing.assert_array_equal(host(sess.canvas)[0], canvas)
+            np.testing.assert_array_equal(host(sess.masked)[0].astype(bool), masked)
+            assert host(sess.steps)[0] == step and host(sess.n_committed)[0] == n
+            if smp.stability_steps:
+                np.testing.assert_array_equal(host(sess.prev_argmax)[0], prev)
+                assert host(sess.stable)[0] == stable
+        steps_seen.append(step)
+        sess.append_block()
+        oracle.append_block(w, TINY, cache, canvas)
+        sync()
+        cache_close(sess, cache, 0, cache.length)
+    if sampler.get("max_transfer"):
+        assert max(steps_seen) >= Lb // 2                   # at most 2 per step: at least 8 steps a block
