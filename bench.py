@@ -15,8 +15,10 @@ The same line carries, under "e2e", the full 32-layer 8B-class model (random
 N(0, 0.02) bf16 weights drawn on the device): block-diffusion decoding at batch
 1 (1024-token prompt) and batch 32 (2048-token prompts), a batch-4 run over a
 65536-position synthetic N(0,1) K/V prefix, greedy causal (AR) decoding and
-greedy linear self-speculation with a rank-128 o_proj adapter, 256 generated
-tokens per sequence each (--no-e2e skips them).
+greedy linear self-speculation with a rank-128 o_proj adapter, and the
+runtime's whole block loop at batch 1 eager and with the anchor-token layout
+replaying a captured graph, 256 generated tokens per sequence each (--no-e2e
+skips them).
 """
 from __future__ import annotations
 
@@ -343,6 +345,31 @@ def e2e_block_diffusion(model, shape, B, T, gen, Lb, max_steps, synthetic_prefix
     return out
 
 
+def e2e_generate(model, shape, B, T, gen, Lb, max_steps, anchor=False, graph_steps=0, seed=1):
+    """The runtime's whole block loop (prefill included): eager, or with the
+    anchor layout and the loop replaying a captured graph of graph_steps steps."""
+    import torch
+
+    import synth
+    from masked_block_diffusion_denoise_amd import runtime as R
+
+    prompt = torch.from_numpy(synth.prompt(shape, B, T, seed=seed)).to(model.device)
+    R.Session(model, B, T + Lb + 64, Lb).generate(prompt, Lb, max_steps, anchor=anchor,
+                                                  graph_steps=graph_steps)  # warm-up
+    sess = R.Session(model, B, T + gen + Lb, Lb)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    _, st = sess.generate(prompt, gen, max_steps, anchor=anchor, graph_steps=graph_steps)
+    torch.cuda.synchronize()
+    total = time.perf_counter() - t0
+    del sess
+    torch.cuda.empty_cache()
+    return {"batch": B, "prompt": T, "generated_per_row": gen, "anchor": anchor, "graph_steps": graph_steps,
+            "e2e_s": round(total, 4), "e2e_tokens_per_s": round(B * gen / total, 2),
+            "denoise_nfe": st.denoise_nfe, "steps_per_block": st.steps_per_block,
+            "tokens_per_forward": round(st.tokens_per_denoise_forward, 3)}
+
+
 def e2e_ar(model, shape, T, n_new, seed=1):
     """Greedy causal decoding at batch 1: prefill, then one-token appends."""
     import torch
@@ -417,6 +444,9 @@ def run_e2e(gen=256) -> dict:
     for name, kw in legs:
         print(f"[bench] e2e {name}", file=sys.stderr, flush=True)
         res[name] = e2e_block_diffusion(model, shape, **kw)
+    for name, kw in (("generate_b1_eager", dict()), ("generate_b1_anchor_graph", dict(anchor=True, graph_steps=31))):
+        print(f"[bench] e2e {name}", file=sys.stderr, flush=True)
+        res[name] = e2e_generate(model, shape, 1, 1024, gen, 32, 32, **kw)
     print("[bench] e2e ar_b1", file=sys.stderr, flush=True)
     res["ar_b1"], ar_tokens = e2e_ar(model, shape, 1024, gen)
     print("[bench] e2e linear_spec_b1", file=sys.stderr, flush=True)

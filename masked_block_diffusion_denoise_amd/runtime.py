@@ -340,6 +340,7 @@ class Session:
     def append_block(self, argmax_out=None, conf_out=None):
         B, Lb = self.B, self.Lb
         ws, n = self.ws.get(self.m.workspace_bytes(B * Lb, self.max_prefix + Lb))
+        argmax_out, conf_out = self._head_pair(argmax_out, conf_out, B * Lb)
         L.call("dlm_append_block", self.m.handle, C.byref(self.kv.c), _p(self.prefix), self.max_prefix,
                _p(self.canvas), B, Lb, _p(argmax_out), _p(conf_out), _p(self.flags), ws, n,
                stream_handle())
@@ -355,12 +356,22 @@ class Session:
 
     # --- driver loop ----------------------------------------------------------
     def generate(self, prompt: torch.Tensor, gen_length: int, max_steps: int, threshold: float = 0.9,
-                 quota: int = 1, sampler: "Sampler | None" = None):
+                 quota: int = 1, sampler: "Sampler | None" = None, anchor: bool = False, graph_steps: int = 0):
         """Prefill, then blocks of denoise+commit until no mask is left, then append.
 
         Rows advance block by block in lockstep; a finished row is frozen until
         every row of the batch has finished its block.  ``sampler`` selects a
-        commit rule other than the native threshold rule.  Returns (tokens [B, G], stats).
+        commit rule other than the native threshold rule.  With ``anchor`` (the
+        MLX guide's native layout, sec. 6) position 0 of each block holds the
+        causal argmax after everything before it -- from the prefill, then from
+        the previous block's post-block pass -- and is not denoised.
+        With ``graph_steps`` = K > 0 the block loop replays a captured HIP graph
+        of K denoise + commit steps and reads the rows' remaining masks once per
+        replay: steps after a block completes leave it unchanged (finished rows
+        are frozen), so they only cost compute.  The graph is captured once with
+        the last block's prefix as the host bound (it sizes the attention grid;
+        each row's actual length is read on the device).
+        Returns (tokens [B, G], stats).
         """
         dev = self.m.device
         tau = torch.full((self.B,), threshold, dtype=torch.float32, device=dev)
@@ -370,25 +381,61 @@ class Session:
             ent = torch.zeros(self.B, self.Lb, dtype=torch.float32, device=dev)
         if sampler is not None:
             sampler.opts(self)  # allocates the adaptive-stopping state before the first block
-        self.prefill(prompt)
+        anc = torch.zeros(self.B, dtype=torch.int32, device=dev) if anchor else None
+        nxt = torch.zeros(self.B, self.Lb, dtype=torch.int32, device=dev) if anchor else None
+        self.prefill(prompt, last_argmax=anc)
         out = []
         st = Stats()
         n_blocks = -(-gen_length // self.Lb)
+
+        def step():
+            self.denoise_step(entropy=ent)
+            if sampler is None:
+                self.commit(tau, q, max_steps)
+            else:
+                self.commit_ex(tau, q, max_steps, sampler, ent)
+
+        graph = None
+        if graph_steps > 0:
+            prefix_now = self.max_prefix
+            self.max_prefix = prefix_now + (n_blocks - 1) * self.Lb  # host bound of every block's step
+            self.ws.get(self.m.workspace_bytes(self.B * self.Lb, self.max_prefix + self.Lb))
+            # one eager step first: every kernel of the step is loaded before the
+            # capture (the first block resets what it touched)
+            self.begin_block()
+            step()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for _ in range(graph_steps):
+                    step()
+            self.max_prefix = prefix_now
         for _ in range(n_blocks):
             self.begin_block()
+            if anchor:
+                self.canvas[:, 0] = anc
+                self.masked[:, 0] = 0
             steps = 0
-            while True:
-                self.denoise_step(entropy=ent)
-                if sampler is None:
-                    self.commit(tau, q, max_steps)
-                else:
-                    self.commit_ex(tau, q, max_steps, sampler, ent)
-                steps += 1
-                st.denoise_nfe += 1
-                st.accepted_tokens += int(self.n_committed.sum().item())
-                if int(self.n_left.max().item()) == 0:
-                    break
-            self.append_block()
+            if graph is not None:
+                while True:
+                    graph.replay()
+                    if int(self.n_left.max().item()) == 0:
+                        break
+                steps = int(self.steps.max().item())
+                st.denoise_nfe += steps
+                st.accepted_tokens += int(self.Lb * self.B - (1 if anchor else 0) * self.B)
+            else:
+                while True:
+                    step()
+                    steps += 1
+                    st.denoise_nfe += 1
+                    st.accepted_tokens += int(self.n_committed.sum().item())
+                    if int(self.n_left.max().item()) == 0:
+                        break
+            if anchor:
+                self.append_block(argmax_out=nxt)
+                anc = nxt[:, -1].clone()
+            else:
+                self.append_block()
             st.post_block_nfe += 1
             st.blocks += 1
             st.steps_per_block.append(steps)

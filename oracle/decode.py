@@ -263,23 +263,30 @@ class BlockStats:
 
 
 def generate_block_diffusion(w, shape, prompt, gen_length, block_length, max_steps,
-                             tau=0.9, quota=1, keep_trace=False, sampler=None):
+                             tau=0.9, quota=1, keep_trace=False, sampler=None, anchor=False):
     """Block-diffusion decoding of one sequence; returns (generated tokens, stats, cache).
 
-    All block positions start as the mask id (no anchor token).  A generation
-    length that is not a multiple of the block length is rounded up.  With
+    All block positions start as the mask id; with ``anchor`` (the MLX guide's
+    native layout, sec. 6) position 0 of each block instead holds the causal
+    argmax after everything before the block -- from the prompt's prefill for
+    the first block, from the previous block's post-block pass after that --
+    and only positions 1..L-1 are denoised.  A generation length that is not a
+    multiple of the block length is rounded up.  With
     ``sampler`` (keyword arguments of ``commit_ex``: rule, min_threshold,
     scaling, entropy_bound, max_transfer, stability_steps, stop_entropy) the
     step uses that commit rule; confidences and entropies are rounded to float32
     first, as the device computes them.
     """
-    cache, _ = prefill(w, shape, prompt)
+    cache, x = prefill(w, shape, prompt)
     n_blocks = -(-gen_length // block_length)
     out = []
     st = BlockStats()
     for _ in range(n_blocks):
         canvas = np.full(block_length, shape.mask_id, dtype=np.int64)
         masked = np.ones(block_length, dtype=bool)
+        if anchor:
+            canvas[0] = int(np.argmax(head_logits(w, shape, x[-1:])[0]))
+            masked[0] = False
         step = 0
         prev, stable = np.full(block_length, -1), 0
         while masked.any():
@@ -300,7 +307,7 @@ def generate_block_diffusion(w, shape, prompt, gen_length, block_length, max_ste
             masked = masked_new
             st.denoise_nfe += 1
             st.accepted_tokens += n
-        append_block(w, shape, cache, canvas)
+        x = append_block(w, shape, cache, canvas)
         st.post_block_nfe += 1
         st.blocks += 1
         st.steps_per_block.append(step)

@@ -406,3 +406,54 @@ def test_tiny_teacher_forced_samplers(sampler):
         cache_close(sess, cache, 0, cache.length)
     if sampler.get("max_transfer"):
         assert max(steps_seen) >= Lb // 2                   # at most 2 per step: at least 8 steps a block
+
+
+def test_tiny_anchor_blocks():
+    """Anchor layout on the device: each block's first token is the causal
+    argmax after everything before it (the oracle's, wherever its top-1 margin
+    is clear), it is never reopened, and a block takes at most L - 1 steps."""
+    announce("tiny anchor blocks")
+    w = synth.model_weights(TINY, seed=0, lm_head_gain=20.0)
+    m = make(TINY, w)
+    prompt = synth.prompt(TINY, 1, 32, seed=2)
+    Lb, max_steps, n_blocks = 16, 16, 3
+    sess = R.Session(m, 1, 128, Lb)
+    out, st = sess.generate(i32(prompt), n_blocks * Lb, max_steps, 0.9, 1, anchor=True)
+    toks = host(out)[0]
+    assert all(s <= Lb - 1 for s in st.steps_per_block), st.steps_per_block
+    assert st.accepted_tokens == n_blocks * (Lb - 1)      # the anchors are not denoised
+    checked = 0
+    for k in range(n_blocks):
+        before = np.concatenate([prompt[0], toks[:k * Lb]])
+        _, x = oracle.prefill(w, TINY, before)
+        lo = oracle.head_logits(w, TINY, x[-1:])[0]
+        top2 = np.sort(lo[np.isfinite(lo)])[-2:]
+        if top2[1] - top2[0] > 5e-2:
+            assert toks[k * Lb] == int(np.argmax(lo)), k
+            checked += 1
+    assert checked >= 2
+    assert (toks != TINY.mask_id).all()
+
+
+@pytest.mark.parametrize("K,anchor,rule", [(4, False, None), (3, True, None), (5, False, "entropy")])
+def test_tiny_graph_replay_equals_eager(K, anchor, rule):
+    """The block loop replaying a captured graph of K steps (eager fills and host
+    reads between the replays) produces exactly the eager loop's tokens and step
+    counts, block after block."""
+    announce(f"tiny graph replay K={K} anchor={anchor} rule={rule}")
+    w = synth.model_weights(TINY, seed=0, lm_head_gain=60.0)
+    m = make(TINY, w)
+    prompt = synth.prompt(TINY, 2, 32, seed=7)
+    Lb, max_steps = 16, 16
+    smp = R.Sampler(rule=rule, entropy_bound=0.5) if rule else None
+    runs = []
+    for gs in (0, K):
+        sess = R.Session(m, 2, 128, Lb)
+        out, st = sess.generate(i32(prompt), 3 * Lb, max_steps, 0.9, 1, sampler=smp, anchor=anchor, graph_steps=gs)
+        sync()
+        runs.append((host(out), st.steps_per_block, st.accepted_tokens, host(sess.prefix)))
+    (o0, s0, a0, p0), (o1, s1, a1, p1) = runs
+    np.testing.assert_array_equal(o1, o0)
+    assert s1 == s0 and a1 == a0
+    np.testing.assert_array_equal(p1, p0)
+    assert (o0 != TINY.mask_id).all()
