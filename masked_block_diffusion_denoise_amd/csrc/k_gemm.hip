@@ -6,14 +6,15 @@
 // an MFMA result holds consecutive output columns of one row and stores them as
 // one vector.
 //
-// One tiled kernel for every shape: 256 x 256, 256 x 128, 256 x 64, 128 x 128
-// or 128 x 64 output tiles, 32- or 64-deep K stages in a ring of LDS buffers
-// filled by direct global-to-LDS loads, each wavefront a block of
-// v_mfma_f32_32x32x16_bf16 tiles.  Short products (one canvas at batch 1-2)
-// are HBM-bound: their activation rows are loaded once per workgroup and shared
-// from LDS, and when there are too few weight tiles to fill the chip K is split
-// over workgroups, the fp32 partials summed in a fixed order by a second kernel
-// (no cross-workgroup atomics or fences).
+// One tiled kernel for every shape: 256 x 256, 256 x 320 (LM head, rows split
+// evenly on the device), 256 x 128, 256 x 64, 128 x 128 or 128 x 64 output
+// tiles, 32- or 64-deep K stages in a ring of LDS buffers filled by direct
+// global-to-LDS loads, each wavefront a block of v_mfma_f32_32x32x16_bf16
+// tiles.  Short products (one canvas at batch 1-2) are HBM-bound: their
+// activation rows are loaded once per workgroup and shared from LDS, and when
+// there are too few weight tiles to fill the chip K is split over workgroups,
+// the fp32 partials summed in a fixed order by a second kernel or by the
+// caller's next step (no cross-workgroup atomics or fences).
 #include <algorithm>
 
 #include "dlm_device.h"
