@@ -77,9 +77,14 @@ class HipEvents:
 
 
 def kernel_source_hash() -> str:
+    """Hash of the GEMM sources without comments and whitespace: the traffic
+    record stays valid across comment-only edits, not across code changes."""
     h = hashlib.sha256()
     for f in ("k_gemm.hip", "dlm_device.h", "dlm_internal.h"):
-        h.update(open(os.path.join(ROOT, "masked_block_diffusion_denoise_amd", "csrc", f), "rb").read())
+        text = open(os.path.join(ROOT, "masked_block_diffusion_denoise_amd", "csrc", f)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update("".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
