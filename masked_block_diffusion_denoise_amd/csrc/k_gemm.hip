@@ -467,12 +467,35 @@ int gemm_head_tile_n(int) { return 256; }
 // 3 splits for 224 tiles, 8 for 32-48 tiles).
 constexpr int SK_BN = 128, SK_BM = 64;
 
+// Long-K products with few 256 x 256 tiles (the down projection at batch 32:
+// 64 tiles, K = 14336) split K so that about one 256 x 256 workgroup per CU
+// runs, instead of 128 x 128 tiles that move twice the bytes per flop
+// (168 -> 145 us).  Other products with few 128 x 128 tiles (QKV and O at
+// batch 4: 48 and 32 tiles) split K over 128 x 128 tiles to about 256
+// workgroups, each K range at least 8 stages (45-50 us -> see DESIGN).
+constexpr int LK_MIN_K = 8192, FEW_TILES = 128;
+
+static bool long_k_split(int M, int N, int K) {
+  return M > SK_BM && N % 256 == 0 && K >= LK_MIN_K && (N / 256) * ((M + 255) / 256) < 256;
+}
+
+static int tiles128(int M, int N) { return (N / 128) * ((M + 127) / 128); }
+
 int gemm_ksplit(int M, int N, int K) {
-  if (M > SK_BM) return 1;
+  if (long_k_split(M, N, K)) {
+    const int tiles = (N / 256) * ((M + 255) / 256);
+    return std::max(1, std::min({(256 + tiles - 1) / tiles, K / (16 * 64), SPLIT_MAX}));
+  }
+  if (M > SK_BM) {
+    const int t = tiles128(M, N);
+    if (t >= FEW_TILES) return 1;
+    return std::max(1, std::min({(256 + t - 1) / t, K / (8 * 64), SPLIT_MAX}));
+  }
   const int tiles = N / SK_BN;
   const int want = (640 + tiles - 1) / tiles;
   return std::max(1, std::min({want, K / (16 * TL_BK), SPLIT_MAX}));
 }
+
 
 size_t gemm_workspace_bytes(int M, int N, int K) {
   const int S = gemm_ksplit(M, N, K);
@@ -488,6 +511,16 @@ static void launch_tiled(const GemmArgs& g, hipStream_t s) {
                      g);
 }
 
+// the partial-product launch of a split product (tile by shape)
+static void launch_partials(const GemmArgs& h, hipStream_t s) {
+  if (long_k_split(h.M, h.N, h.K))
+    launch_tiled<EPI_SPLITK, 256, 256, 4, 2, 2, 64>(h, s);
+  else if (h.M > SK_BM)
+    launch_tiled<EPI_SPLITK, 128, 128, 2, 2, 3, 64>(h, s);
+  else
+    launch_tiled<EPI_SPLITK, SK_BN, SK_BM, 4, 1, 3, 64>(h, s);
+}
+
 template <int EPI>
 static hipError_t launch_epi(const GemmArgs& g, hipStream_t s) {
   if constexpr (EPI == EPI_HEAD) {
@@ -499,7 +532,7 @@ static hipError_t launch_epi(const GemmArgs& g, hipStream_t s) {
     // split evenly are both launched, and only the one needing fewer row tiles
     // runs (e.g. 530 rows: two tiles of 288 rows instead of three).
     if (g.M <= 64) {
-      launch_tiled<EPI, 256, 64, 4, 1, 3>(g, s);
+      launch_tiled<EPI, 256, 64, 4, 1, 4>(g, s);  // 4 stages: 194 vs 202 us with 3 (6: 212)
     } else if (g.M <= 128) {
       launch_tiled<EPI, 256, 128, 4, 2, 3>(g, s);
     } else {
@@ -511,18 +544,15 @@ static hipError_t launch_epi(const GemmArgs& g, hipStream_t s) {
         launch_tiled<EPI, 256, 320, 4, 2, 2, 64, true>(h, s);
       }
     }
+  } else if (gemm_ksplit(g.M, g.N, g.K) > 1) {
+    if (!g.kpart) return hipErrorInvalidValue;
+    GemmArgs h = g;
+    h.ksplit = gemm_ksplit(g.M, g.N, g.K);
+    launch_partials(h, s);
+    const int cols = EPI == EPI_SWIGLU ? g.N / 2 : g.N;
+    hipLaunchKernelGGL((k_splitk_reduce<EPI>), dim3((g.M * (cols / 4) + 255) / 256), dim3(256), 0, s, h);
   } else if (g.M <= SK_BM) {
-    const int S = gemm_ksplit(g.M, g.N, g.K);
-    if (S > 1) {
-      if (!g.kpart) return hipErrorInvalidValue;
-      GemmArgs h = g;
-      h.ksplit = S;
-      launch_tiled<EPI_SPLITK, SK_BN, SK_BM, 4, 1, 3, 64>(h, s);
-      const int cols = EPI == EPI_SWIGLU ? g.N / 2 : g.N;
-      hipLaunchKernelGGL((k_splitk_reduce<EPI>), dim3((g.M * (cols / 4) + 255) / 256), dim3(256), 0, s, h);
-    } else {
-      launch_tiled<EPI, SK_BN, SK_BM, 4, 1, 3, 64>(g, s);
-    }
+    launch_tiled<EPI, SK_BN, SK_BM, 4, 1, 3, 64>(g, s);
   } else {
     // 256 x 256 tiles where they still give at least one wave of workgroups
     // (the SwiGLU gate/up projection); 128 x 128 otherwise: with at most one
@@ -544,7 +574,7 @@ hipError_t gemm_partials(const GemmArgs& g, hipStream_t s) {
   if (g.M <= 0 || S <= 1 || !g.kpart) return hipErrorInvalidValue;
   GemmArgs h = g;
   h.ksplit = S;
-  launch_tiled<EPI_SPLITK, SK_BN, SK_BM, 4, 1, 3, 64>(h, s);
+  launch_partials(h, s);
   return hipGetLastError();
 }
 
