@@ -128,7 +128,9 @@ __global__ void __launch_bounds__(GS * 64) k_attn(AttnArgs a, int chunk_len) {
   const int split = blockIdx.x, qb = blockIdx.y;
   const int b = blockIdx.z / a.G, g = blockIdx.z % a.G;
   const int h = g * GS + w;
-  const int p0 = (a.prefix ? a.prefix[b] : 0) + a.pos_offset;
+  // uniform over the workgroup (kept in scalar registers, so the per-stage
+  // tests below are scalar branches)
+  const int p0 = __builtin_amdgcn_readfirstlane((a.prefix ? a.prefix[b] : 0) + a.pos_offset);
   const int kv_len = min(p0 + a.Lq, a.cap);  // never read past the cache
   const int jq = qb * 32 + (lane & 31);      // this lane's query (block-relative)
   const int half = lane >> 5;
@@ -214,17 +216,33 @@ __global__ void __launch_bounds__(GS * 64) k_attn(AttnArgs a, int chunk_len) {
     if (st + 1 < nst) issue(st + 1);
     const int k0 = kbeg + st * SUB * KT;
     const uint32_t sb = lbase + (st & 1) * STAGE;
+    // The stage that reaches past the range (the last one): cache slots past the
+    // row's end may hold anything (also NaN), and a tile past the range was not
+    // loaded, so their values are zeroed in LDS -- a zero probability alone
+    // would still give 0 * NaN.  No load is in flight on the last stage.
+    const bool tail = k0 + SUB * KT > kend;
+    if (tail) {
+      uint8_t* st_lds = lds + (st & 1) * STAGE;
+      const int first = max(0, kend - k0);  // first stage key past the range
+      for (int i = threadIdx.x; i < (SUB * KT - first) * HD; i += GS * 64) {
+        const int kk = first + i / HD, d = i % HD;      // stage key, value dim
+        const int u = kk / KT, c = (kk % KT) / 16, vrow = c * HD + d;
+        const int ph = ((kk % 16) / 8) ^ vxor(vrow);  // physical 16-byte half
+        *reinterpret_cast<uint16_t*>(st_lds + u * TILE + TILE_K + (vrow * 2 + ph) * 16 + (kk % 8) * 2) = 0;
+      }
+      __syncthreads();
+    }
 
-    // S of the SUB tiles: two independent accumulation chains per tile (even /
-    // odd steps); fragment reads in batches of KB steps per tile (register
-    // pressure), KB even so that each batch feeds both chains
-    f32x16 sacc[SUB], sodd[SUB];
+    // S of the SUB tiles: one accumulation chain per tile, the chains
+    // interleaved so that consecutive MFMAs are independent; fragment reads in
+    // batches of KB steps per tile (register pressure)
+    f32x16 sacc[SUB];
 #pragma unroll
     for (int u = 0; u < SUB; ++u)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[u][r] = sodd[u][r] = 0.f;
+      for (int r = 0; r < 16; ++r) sacc[u][r] = 0.f;
     constexpr int KB = NS >= 8 ? NS / 2 : NS;
-    static_assert(KB % 2 == 0 && NS % KB == 0, "batches of an even number of K fragments");
+    static_assert(NS % KB == 0, "whole batches of K fragments");
 #pragma unroll
     for (int hs = 0; hs < NS; hs += KB) {
       uint32_t ka[SUB * KB];
@@ -235,40 +253,41 @@ __global__ void __launch_bounds__(GS * 64) k_attn(AttnArgs a, int chunk_len) {
         for (int s = 0; s < KB; ++s) ka[u * KB + s] = sb + u * TILE + koff[hs + s];
       lds_read_n<SUB * KB>(ka, kf);
 #pragma unroll
-      for (int s = 0; s < KB; s += 2)
+      for (int s = 0; s < KB; ++s)
 #pragma unroll
-        for (int u = 0; u < SUB; ++u) {
-          sacc[u] = mfma32x32x16(as_bf16x8(kf[u * KB + s]), qf[hs + s], sacc[u]);
-          sodd[u] = mfma32x32x16(as_bf16x8(kf[u * KB + s + 1]), qf[hs + s + 1], sodd[u]);
-        }
+        for (int u = 0; u < SUB; ++u) sacc[u] = mfma32x32x16(as_bf16x8(kf[u * KB + s]), qf[hs + s], sacc[u]);
     }
     // register r of tile u holds key k0 + u*KT + 16*(r/8) + 8*half + (r%8).
-    // Only the last tiles of the range and causal passes need a mask.
-    bool tail[SUB];
+    // Only the last stage of the range and causal passes need a mask.
+    // A key is masked when it is past the range or (causal) after the query:
+    // key >= min(kend, qpos + 1), one compare against a per-lane limit.  The
+    // empty asm keeps the masking behind its branch (if-converted, it would run
+    // on every stage).
+    if (tail || a.causal) {
+      asm volatile("");
+      const int lim = (a.causal ? min(kend, qpos + 1) : kend) - (k0 + 8 * half);
+#pragma unroll
+      for (int u = 0; u < SUB; ++u)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (u * KT + 16 * (r >> 3) + (r & 7) >= lim) sacc[u][r] = -INFINITY;
+    }
+    // this lane's maximum over its half of the stage's keys (lanes l and l^32
+    // hold the two halves of one query)
     float mloc = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < SUB; ++u) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[u][r] += sodd[u][r];
-      const int ku = k0 + u * KT;
-      tail[u] = ku + KT > kend;
-      if (tail[u] || a.causal) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = ku + 16 * (r >> 3) + 8 * half + (r & 7);
-          if (key >= kend || (a.causal && key > qpos)) sacc[u][r] = -INFINITY;
-        }
-      }
+    for (int u = 0; u < SUB; ++u)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[u][r]);
-    }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, WAVE)) * scale;
+    mloc *= scale;
     // Lazy rescaling: the exponent reference m_run only moves when some query of
     // the wavefront sees a score more than 2^RESCALE above it (then all lanes
     // rescale together); otherwise p <= 2^RESCALE and the output accumulators
-    // are not touched.  o / l is unchanged by the choice.
+    // are not touched.  o / l is unchanged by the choice.  The two halves of a
+    // query keep the same m_run: the test is over the whole wavefront, and the
+    // new reference takes the maximum over both halves.
     if (__any(mloc > m_run + RESCALE)) {
-      const float m_new = fmaxf(m_run, mloc);
+      const float m_new = fmaxf(m_run, fmaxf(mloc, __shfl_xor(mloc, 32, WAVE)));
       const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
@@ -278,6 +297,7 @@ __global__ void __launch_bounds__(GS * 64) k_attn(AttnArgs a, int chunk_len) {
       m_run = m_new;
     }
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    // l_run is this lane's half of the query's sum; the halves are added at the end
     float lsum = 0.f;
     bf16x8 pb[SUB][2];
 #pragma unroll
@@ -296,11 +316,8 @@ __global__ void __launch_bounds__(GS * 64) k_attn(AttnArgs a, int chunk_len) {
         pb[u][c] = as_bf16x8(x);
       }
     }
-    lsum += __shfl_xor(lsum, 32, WAVE);
     l_run += lsum;
-    // cache slots past the row's end may hold anything (also NaN), and a tile
-    // past the range was not loaded: their values are zeroed in the fragments,
-    // not only their probabilities
+    // O^T += V^T P^T; consecutive MFMAs go to different output blocks
     constexpr int DH = ND > 1 ? ND / 2 : 1;  // output blocks per batch of V reads
 #pragma unroll
     for (int d0 = 0; d0 < ND; d0 += DH) {
@@ -317,25 +334,14 @@ __global__ void __launch_bounds__(GS * 64) k_attn(AttnArgs a, int chunk_len) {
 #pragma unroll
       for (int u = 0; u < SUB; ++u)
 #pragma unroll
-        for (int dd = 0; dd < DH; ++dd)
+        for (int c = 0; c < 2; ++c)
 #pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            u32x4 x4 = vf[(u * DH + dd) * 2 + c];
-            if (tail[u]) {
-              const int valid = kend - (k0 + u * KT + 16 * c + 8 * half);  // keys of this fragment in range
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                uint32_t x = x4[e];
-                if (2 * e >= valid) x &= 0xffff0000u;
-                if (2 * e + 1 >= valid) x &= 0x0000ffffu;
-                x4[e] = x;
-              }
-            }
-            o[d0 + dd] = mfma32x32x16(as_bf16x8(x4), pb[u][c], o[d0 + dd]);
-          }
+          for (int dd = 0; dd < DH; ++dd)
+            o[d0 + dd] = mfma32x32x16(as_bf16x8(vf[(u * DH + dd) * 2 + c]), pb[u][c], o[d0 + dd]);
     }
   }
 
+  l_run += __shfl_xor(l_run, 32, WAVE);
   // lane holds O^T[d][query]: d = dc*32 + 8*(r/4) + 4*half + r%4
   if (jq >= a.Lq) return;
   if (splits == 1) {
