@@ -38,10 +38,10 @@ namespace dlm {
 
 constexpr int KT = 32;          // keys per tile
 constexpr int MIN_CHUNK = 256;  // minimum keys per split (8 tiles)
-// Launch shape: about 512 workgroups (two per CU), each with a 3-stage ring, so
-// that the other workgroup on a CU hides the latency of a tile's dependent chain
-// (one workgroup per CU with a deeper ring measured up to 25% slower at batch 4
-// over a 65536-position prefix, and no faster at batch 1).
+// Launch shape: about 512 workgroups (two per CU, each with its 64 KB ring), so
+// that the other workgroup on a CU hides the latency of a stage's dependent
+// chain (one workgroup per CU with a deeper ring measured up to 25% slower at
+// batch 4 over a 65536-position prefix, and no faster at batch 1).
 constexpr int TARGET_WG = 512;
 constexpr int SUB = 2;  // 32-key tiles per ring stage (two stages in the ring)
 constexpr float RESCALE = 8.f;  // lazy-rescale threshold (log2 units)
@@ -370,7 +370,9 @@ __global__ void __launch_bounds__(GS * 64) k_attn(AttnArgs a, int chunk_len) {
 
 // Merge split partials: o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
 // One wavefront per (row, head): lane s holds split s's (m, l); each lane sums
-// HD/64 (or one) output dims over the splits in split order.
+// HD/64 (or one) output dims over the splits in split order, the partials of
+// eight splits loaded at once (every split's partial is written, an empty one
+// as zeros with weight 0).
 template <int HD>
 __global__ void __launch_bounds__(256) k_attn_merge(AttnArgs a, int splits) {
   const int rows = a.B * a.Lq;
@@ -388,19 +390,28 @@ __global__ void __launch_bounds__(256) k_attn_merge(AttnArgs a, int splits) {
   const float wgt = (ml.y > 0.f) ? __builtin_amdgcn_exp2f(ml.x - mu) : 0.f;
   const float l = wave_sum(wgt * ml.y);
   constexpr int PER = HD >= 64 ? HD / 64 : 1;
+  constexpr int B8 = 8;
   float acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-  const int d0 = lane * PER;
-  for (int s = 0; s < splits; ++s) {
-    const float ws = __shfl(wgt, s, WAVE);
-    if (ws != 0.f && d0 < HD) {
-      const float* po = a.part_o + at(s) * HD + d0;
+  const int d0 = min(lane * PER, HD - PER);  // lanes past HD (HD < 64) duplicate the last dims, not stored
+  for (int s0 = 0; s0 < splits; s0 += B8) {
+    float v[B8][PER];
 #pragma unroll
-      for (int e = 0; e < PER; ++e) acc[e] += ws * po[e];
+    for (int k = 0; k < B8; ++k) {
+      const float* po = a.part_o + at(min(s0 + k, splits - 1)) * HD + d0;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) v[k][e] = po[e];
+    }
+#pragma unroll
+    for (int k = 0; k < B8; ++k) {
+      const float ws = __shfl(wgt, min(s0 + k, 63), WAVE);
+      if (s0 + k < splits)
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[e] += ws * v[k][e];
     }
   }
-  if (d0 < HD) {
+  if (lane * PER < HD) {
     bf16_t* op = static_cast<bf16_t*>(a.o) + static_cast<size_t>(mrow) * a.H * HD + h * HD + d0;
 #pragma unroll
     for (int e = 0; e < PER; ++e) op[e] = f32_to_bf16(l > 0.f ? acc[e] / l : 0.f);

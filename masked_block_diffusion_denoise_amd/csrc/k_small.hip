@@ -282,51 +282,77 @@ __global__ void __launch_bounds__(256) k_rmsnorm(const float* __restrict__ x, in
   }
 }
 
+// Sum over a workgroup of T threads (wave sums, then the waves in order).
+template <int T>
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int i = 0; i < T / 64; ++i) t += red[i];
+  return t;
+}
+
 // Residual update from K-split partials fused with the next RMSNorm:
 // x[m] += sum_s part[s][m] (split order), then xn[m] = RMSNorm(x[m]) * g.  One
-// block per row; a thread re-reads only the x values it wrote itself.
-__global__ void __launch_bounds__(256) k_resid_norm(const float* __restrict__ part, int S, int M,
-                                                    float* __restrict__ x, int d, const bf16_t* __restrict__ g,
-                                                    float eps, bf16_t* __restrict__ xn) {
-  __shared__ float red[4];
-  const int m = blockIdx.x;
+// workgroup per row, one thread per 8 columns (d / 8 threads, at most 1024):
+// every load of the row (the residual and its S partials) is issued at once and
+// the updated row stays in registers for the normalisation.
+template <int T>
+__global__ void __launch_bounds__(T) k_resid_norm(const float* __restrict__ part, int S, int M,
+                                                  float* __restrict__ x, int d, const bf16_t* __restrict__ g,
+                                                  float eps, bf16_t* __restrict__ xn) {
+  __shared__ float red[T / 64];
+  const int m = blockIdx.x, c = threadIdx.x;
+  const bool on = c < d / 8;
   const size_t plane = static_cast<size_t>(M) * d;
   float* xr = x + static_cast<size_t>(m) * d;
   const float* pr = part + static_cast<size_t>(m) * d;
+  float4 v0 = make_float4(0.f, 0.f, 0.f, 0.f), v1 = v0;
   float ss = 0.f;
-  for (int c = threadIdx.x; c < d / 8; c += 256) {
-    float4 v0 = reinterpret_cast<const float4*>(xr)[2 * c];
-    float4 v1 = reinterpret_cast<const float4*>(xr)[2 * c + 1];
+  if (on) {
+    v0 = reinterpret_cast<const float4*>(xr)[2 * c];
+    v1 = reinterpret_cast<const float4*>(xr)[2 * c + 1];
     const float4 a0 = sum_planes(pr + 8 * c, plane, S);
     const float4 a1 = sum_planes(pr + 8 * c + 4, plane, S);
     v0.x += a0.x; v0.y += a0.y; v0.z += a0.z; v0.w += a0.w;
     v1.x += a1.x; v1.y += a1.y; v1.z += a1.z; v1.w += a1.w;
     reinterpret_cast<float4*>(xr)[2 * c] = v0;
     reinterpret_cast<float4*>(xr)[2 * c + 1] = v1;
-    ss += v0.x * v0.x + v0.y * v0.y + v0.z * v0.z + v0.w * v0.w + v1.x * v1.x + v1.y * v1.y + v1.z * v1.z +
-          v1.w * v1.w;
+    ss = v0.x * v0.x + v0.y * v0.y + v0.z * v0.z + v0.w * v0.w + v1.x * v1.x + v1.y * v1.y + v1.z * v1.z +
+         v1.w * v1.w;
   }
-  const float rstd = rsqrtf(block_sum_256(ss, red) / d + eps);
-  for (int c = threadIdx.x; c < d / 8; c += 256) {
-    const float4 v0 = reinterpret_cast<const float4*>(xr)[2 * c];
-    const float4 v1 = reinterpret_cast<const float4*>(xr)[2 * c + 1];
-    float gg[8];
-    unpack8(ld16(g + c * 8), gg);
-    u32x4 o;
-    o[0] = pack_bf16x2(v0.x * rstd * gg[0], v0.y * rstd * gg[1]);
-    o[1] = pack_bf16x2(v0.z * rstd * gg[2], v0.w * rstd * gg[3]);
-    o[2] = pack_bf16x2(v1.x * rstd * gg[4], v1.y * rstd * gg[5]);
-    o[3] = pack_bf16x2(v1.z * rstd * gg[6], v1.w * rstd * gg[7]);
-    st16(xn + static_cast<size_t>(m) * d + c * 8, o);
-  }
+  const float rstd = rsqrtf(block_sum<T>(ss, red) / d + eps);
+  if (!on) return;
+  float gg[8];
+  unpack8(ld16(g + c * 8), gg);
+  u32x4 o;
+  o[0] = pack_bf16x2(v0.x * rstd * gg[0], v0.y * rstd * gg[1]);
+  o[1] = pack_bf16x2(v0.z * rstd * gg[2], v0.w * rstd * gg[3]);
+  o[2] = pack_bf16x2(v1.x * rstd * gg[4], v1.y * rstd * gg[5]);
+  o[3] = pack_bf16x2(v1.z * rstd * gg[6], v1.w * rstd * gg[7]);
+  st16(xn + static_cast<size_t>(m) * d + c * 8, o);
 }
 
 hipError_t resid_norm(const float* part, int S, int M, float* x, int d, const void* gain, float eps, void* xn,
                       hipStream_t s) {
   if (M <= 0) return hipSuccess;
-  if (S < 1 || S > SPLIT_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_resid_norm, dim3(M), dim3(256), 0, s, part, S, M, x, d, static_cast<const bf16_t*>(gain),
-                     eps, static_cast<bf16_t*>(xn));
+  if (S < 1 || S > SPLIT_MAX || d % 8 || d / 8 > 1024) return hipErrorInvalidValue;
+  auto go = [&](auto kern, int T) {
+    hipLaunchKernelGGL(kern, dim3(M), dim3(T), 0, s, part, S, M, x, d, static_cast<const bf16_t*>(gain), eps,
+                       static_cast<bf16_t*>(xn));
+  };
+  const int need = d / 8;
+  if (need <= 64)
+    go(k_resid_norm<64>, 64);
+  else if (need <= 256)
+    go(k_resid_norm<256>, 256);
+  else if (need <= 512)
+    go(k_resid_norm<512>, 512);
+  else
+    go(k_resid_norm<1024>, 1024);
   return hipGetLastError();
 }
 
