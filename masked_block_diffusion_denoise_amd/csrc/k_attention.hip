@@ -38,10 +38,11 @@ namespace dlm {
 
 constexpr int KT = 32;          // keys per tile
 constexpr int MIN_CHUNK = 256;  // minimum keys per split (8 tiles)
-// Launch shape: about 512 workgroups (two per CU, each with its 64 KB ring), so
+// Launch shape: up to 512 workgroups (two per CU, each with its 64 KB ring), so
 // that the other workgroup on a CU hides the latency of a stage's dependent
 // chain (one workgroup per CU with a deeper ring measured up to 25% slower at
-// batch 4 over a 65536-position prefix, and no faster at batch 1).
+// batch 4 over a 65536-position prefix, and no faster at batch 1); key splits
+// are only made for that second workgroup while they stay long (attn_splits).
 constexpr int TARGET_WG = 512;
 constexpr int SUB = 2;  // 32-key tiles per ring stage (two stages in the ring)
 constexpr float RESCALE = 8.f;  // lazy-rescale threshold (log2 units)
@@ -419,15 +420,23 @@ __global__ void __launch_bounds__(256) k_attn_merge(AttnArgs a, int splits) {
 }
 
 // Key splits: enough (row, group, query block, split) workgroups for about one
-// per CU, each split at least MIN_CHUNK keys; no split when the batch already
-// fills the chip (the merge costs a pass over fp32 partials).  At most 64 splits
-// (one merge lane each).
+// per CU, each split at least MIN_CHUNK keys; two per CU (about TARGET_WG in
+// all) only while every split keeps at least LONG_CHUNK keys.  A split costs a
+// pass over fp32 partials (written here, read by the merge): with ~2000 keys
+// per split (batch 32 over 4096 positions) that outweighs the second workgroup
+// (133 vs 109-123 us unsplit); with ~4000 (batch 4 over 65536) it does not
+// (212 vs 224 us with one workgroup per CU).  At most 64 splits (one merge
+// lane each).
+constexpr int LONG_CHUNK = 3072;
+
 int attn_splits(const AttnArgs& a, int* chunk_out) {
   const int qblocks = (a.Lq + 31) / 32;
   const long base = static_cast<long>(qblocks) * a.B * a.G;
-  int splits = static_cast<int>((TARGET_WG + base - 1) / base);
-  const int max_splits = std::max(1, a.max_kv / MIN_CHUNK);
-  splits = std::max(1, std::min({splits, max_splits, 64}));
+  const int max_splits = std::max(1, std::min(a.max_kv / MIN_CHUNK, 64));
+  auto want = [&](long wgs) { return static_cast<int>(std::min<long>(max_splits, std::max<long>(1, (wgs + base - 1) / base))); };
+  int splits = want(TARGET_WG / 2);
+  const int two = want(TARGET_WG);
+  if (two > splits && a.max_kv / two >= LONG_CHUNK) splits = two;
   int chunk = (a.max_kv + splits - 1) / splits;
   chunk = (chunk + KT - 1) / KT * KT;
   splits = (a.max_kv + chunk - 1) / chunk;
