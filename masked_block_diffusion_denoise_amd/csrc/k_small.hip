@@ -384,82 +384,95 @@ hipError_t rope_table(const int* prefix, int pos_offset, int B, int Lq, int hd, 
 // from bf16 qkv (rotated query heads are written back in place) or, with PART,
 // from fp32 K-split partials [S][M][(H+2G)hd] summed in split order (the query
 // heads are then written to qkv, rounded to bf16 once, after the rotation).
-// Each thread handles four rotation pairs of one head.  K cache [B][G][cap][hd];
-// V cache [B][G][cap/16][hd][16] (blocks of 16 positions, position fastest).
+// K cache [B][G][cap][hd]; V cache [B][G][cap/16][hd][16] (blocks of 16
+// positions, position fastest).
+//
+// One workgroup = 16 consecutive rows x one head.  Query and key heads: a thread
+// takes four rotation pairs of one row.  Value heads: a thread takes 8 dims of
+// one row, consecutive threads consecutive rows, so the 16 rows' values of one
+// dim (consecutive positions of a batch row) are one contiguous run of the
+// blocked V cache instead of 16 scattered 2-byte stores.
+constexpr int RK_ROWS = 16;
+
 template <bool PART>
 __global__ void __launch_bounds__(256) k_rope_kv(bf16_t* __restrict__ qkv, const float* __restrict__ part, int S,
                                                  int M, int Lq, int H, int G, int hd,
                                                  const float2* __restrict__ tab, bf16_t* __restrict__ kc,
                                                  bf16_t* __restrict__ vc, const int* __restrict__ prefix,
                                                  int off, int cap) {
-  const int m = blockIdx.x;
+  const int h = blockIdx.y, t = threadIdx.x;
   const int half = hd / 2, quads = half / 4;
   const int nh = H + 2 * G;
-  const int b = m / Lq, j = m % Lq;
-  const int pos = (prefix ? prefix[b] : 0) + off + j;
-  const bool slot_ok = pos >= 0 && pos < cap;
-  bf16_t* row = qkv + static_cast<size_t>(m) * nh * hd;
   const size_t plane = static_cast<size_t>(M) * nh * hd;
-  const float* prow = PART ? part + static_cast<size_t>(m) * nh * hd : nullptr;
-  // four consecutive values of the row from column c
-  auto load4 = [&](int c, float* v) {
+  // four consecutive values of row m from column c
+  auto load4 = [&](int m, int c, float* v) {
     if constexpr (PART) {
-      const float4 acc = sum_planes(prow + c, plane, S);
+      const float4 acc = sum_planes(part + static_cast<size_t>(m) * nh * hd + c, plane, S);
       v[0] = acc.x; v[1] = acc.y; v[2] = acc.z; v[3] = acc.w;
     } else {
-      const u32x2 u = *reinterpret_cast<const u32x2*>(row + c);
+      const u32x2 u = *reinterpret_cast<const u32x2*>(qkv + static_cast<size_t>(m) * nh * hd + c);
       v[0] = __uint_as_float(u[0] << 16);
       v[1] = __uint_as_float(u[0] & 0xffff0000u);
       v[2] = __uint_as_float(u[1] << 16);
       v[3] = __uint_as_float(u[1] & 0xffff0000u);
     }
   };
-  // one (head, quad) task per thread; blockIdx.y picks 256 of the row's tasks
-  {
-    const int t = blockIdx.y * blockDim.x + threadIdx.x;
-    if (t >= nh * quads) return;
-    const int h = t / quads, i0 = (t % quads) * 4;
-    float x1[4], x2[4];
-    load4(h * hd + i0, x1);
-    load4(h * hd + i0 + half, x2);
-    if (h >= H + G) {  // value head: to the blocked V cache
-      if (!slot_ok) return;
-      const int g = h - H - G;
-      bf16_t* vb = vc + ((static_cast<size_t>(b) * G + g) * (cap / 16) + pos / 16) * hd * 16 + pos % 16;
+  auto slot = [&](int m, int& b, int& pos) {
+    b = m / Lq;
+    pos = (prefix ? prefix[b] : 0) + off + m % Lq;
+    return pos >= 0 && pos < cap;
+  };
+  if (h >= H + G) {  // value head: 8 dims of one row per thread, rows fastest
+    const int r = t % RK_ROWS, c = t / RK_ROWS;
+    const int m = blockIdx.x * RK_ROWS + r;
+    if (m >= M || c >= hd / 8) return;
+    int b, pos;
+    if (!slot(m, b, pos)) return;
+    float x[8];
+    load4(m, h * hd + 8 * c, x);
+    load4(m, h * hd + 8 * c + 4, x + 4);
+    const int g = h - H - G;
+    bf16_t* vb = vc + ((static_cast<size_t>(b) * G + g) * (cap / 16) + pos / 16) * hd * 16 + pos % 16;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        vb[(i0 + u) * 16] = f32_to_bf16(x1[u]);
-        vb[(i0 + u + half) * 16] = f32_to_bf16(x2[u]);
-      }
-      return;
-    }
-    float y1[4], y2[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float2 cs = tab[static_cast<size_t>(m) * half + i0 + u];
-      y1[u] = x1[u] * cs.x - x2[u] * cs.y;
-      y2[u] = x2[u] * cs.x + x1[u] * cs.y;
-    }
-    const u32x2 olo = {pack_bf16x2(y1[0], y1[1]), pack_bf16x2(y1[2], y1[3])};
-    const u32x2 ohi = {pack_bf16x2(y2[0], y2[1]), pack_bf16x2(y2[2], y2[3])};
-    if (h < H) {
-      bf16_t* hp = row + h * hd;
-      *reinterpret_cast<u32x2*>(hp + i0) = olo;
-      *reinterpret_cast<u32x2*>(hp + i0 + half) = ohi;
-    } else if (slot_ok) {
-      const int g = h - H;
-      bf16_t* kp = kc + ((static_cast<size_t>(b) * G + g) * cap + pos) * hd;
-      *reinterpret_cast<u32x2*>(kp + i0) = olo;
-      *reinterpret_cast<u32x2*>(kp + i0 + half) = ohi;
-    }
+    for (int u = 0; u < 8; ++u) vb[(8 * c + u) * 16] = f32_to_bf16(x[u]);
+    return;
   }
+  // query or key head: four rotation pairs of one row per thread
+  const int r = t / quads, i0 = (t % quads) * 4;
+  const int m = blockIdx.x * RK_ROWS + r;
+  if (r >= RK_ROWS || m >= M) return;
+  float x1[4], x2[4];
+  load4(m, h * hd + i0, x1);
+  load4(m, h * hd + i0 + half, x2);
+  float y1[4], y2[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const float2 cs = tab[static_cast<size_t>(m) * half + i0 + u];
+    y1[u] = x1[u] * cs.x - x2[u] * cs.y;
+    y2[u] = x2[u] * cs.x + x1[u] * cs.y;
+  }
+  const u32x2 olo = {pack_bf16x2(y1[0], y1[1]), pack_bf16x2(y1[2], y1[3])};
+  const u32x2 ohi = {pack_bf16x2(y2[0], y2[1]), pack_bf16x2(y2[2], y2[3])};
+  if (h < H) {
+    bf16_t* hp = qkv + static_cast<size_t>(m) * nh * hd + h * hd;
+    *reinterpret_cast<u32x2*>(hp + i0) = olo;
+    *reinterpret_cast<u32x2*>(hp + i0 + half) = ohi;
+    return;
+  }
+  int b, pos;
+  if (!slot(m, b, pos)) return;
+  const int g = h - H;
+  bf16_t* kp = kc + ((static_cast<size_t>(b) * G + g) * cap + pos) * hd;
+  *reinterpret_cast<u32x2*>(kp + i0) = olo;
+  *reinterpret_cast<u32x2*>(kp + i0 + half) = ohi;
 }
 
 hipError_t rope_kv(void* qkv, int M, int Lq, int H, int G, int hd, const float2* tab, void* kc, void* vc,
                    const int* prefix, int pos_offset, int cap, hipStream_t s, const float* part, int S) {
   if (M <= 0) return hipSuccess;
   if (part && (S < 1 || S > SPLIT_MAX)) return hipErrorInvalidValue;
-  const dim3 grid(M, ((H + 2 * G) * (hd / 8) + 255) / 256);
+  if (hd % 8 || RK_ROWS * (hd / 8) > 256) return hipErrorInvalidValue;
+  const dim3 grid((M + RK_ROWS - 1) / RK_ROWS, H + 2 * G);
   if (part)
     hipLaunchKernelGGL(k_rope_kv<true>, grid, dim3(256), 0, s, static_cast<bf16_t*>(qkv), part, S, M, Lq, H, G,
                        hd, tab, static_cast<bf16_t*>(kc), static_cast<bf16_t*>(vc), prefix, pos_offset, cap);
