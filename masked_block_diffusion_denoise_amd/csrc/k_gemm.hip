@@ -114,6 +114,11 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 __device__ __forceinline__ void load_lds16(const void* src, void* lds_dst) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
 }
+// The same marked non-temporal (cache policy NT): lines that are read once are
+// evicted first, so they do not push out cached data of later kernels.
+__device__ __forceinline__ void load_lds16_nt(const void* src, void* lds_dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 2);
+}
 
 // Wait until at most N of this wavefront's vector-memory operations are
 // outstanding, then join the workgroup barrier.
@@ -265,11 +270,21 @@ __global__ void __launch_bounds__(WN * WM * 64) k_gemm_tiled(GemmArgs g) {
   // this workgroup's stages: [k_lo, k_lo + nk) of the K / 32 stages
   const int k_lo = split * (g.K / BK) / S;
   const int nk = (split + 1) * (g.K / BK) / S - k_lo;
+  // The split partial products of short row counts (one canvas at batch 1-2)
+  // read every weight exactly once: those weight loads are non-temporal (the
+  // 8B-class full model at batch 1: 4.32 -> 4.27 ms per denoise step over a
+  // 1024-position prefix, 4.49 -> 4.31 over 4096; for the LM head and the
+  // batch-32 tiles, which reuse weight tiles across row tiles, it was slower).
+  constexpr bool NT_W = EPI == EPI_SPLITK && BM <= 64;
   auto issue = [&](int kt) {  // kt counts this workgroup's stages from 0
     uint8_t* dst = lds + (kt % NBUF) * STAGE + w * BLK * 1024;
 #pragma unroll
-    for (int b = 0; b < BLK; ++b)
-      load_lds16(src[b] + (k_lo + kt) * BK, dst + b * 1024);
+    for (int b = 0; b < BLK; ++b) {
+      if (NT_W && (w * BLK + b) * 1024 / ROW < BN)  // a weight block
+        load_lds16_nt(src[b] + (k_lo + kt) * BK, dst + b * 1024);
+      else
+        load_lds16(src[b] + (k_lo + kt) * BK, dst + b * 1024);
+    }
   };
 
   f32x16 acc[TN][TM];

@@ -554,7 +554,7 @@ __global__ void __launch_bounds__(256) k_head_merge(const float4* __restrict__ p
   si[threadIdx.x] = acc.idx;
   __syncthreads();
   for (int w = 128; w > 0; w >>= 1) {
-    if (threadIdx.x < w) {
+    if (static_cast<int>(threadIdx.x) < w) {
       MaxSumIdx a{sm[threadIdx.x], ss[threadIdx.x], si[threadIdx.x], st[threadIdx.x]};
       MaxSumIdx c{sm[threadIdx.x + w], ss[threadIdx.x + w], si[threadIdx.x + w], st[threadIdx.x + w]};
       a = msi_combine(a, c);
