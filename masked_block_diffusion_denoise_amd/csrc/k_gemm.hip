@@ -270,12 +270,16 @@ __global__ void __launch_bounds__(WN * WM * 64) k_gemm_tiled(GemmArgs g) {
   // this workgroup's stages: [k_lo, k_lo + nk) of the K / 32 stages
   const int k_lo = split * (g.K / BK) / S;
   const int nk = (split + 1) * (g.K / BK) / S - k_lo;
-  // The split partial products of short row counts (one canvas at batch 1-2)
-  // read every weight exactly once: those weight loads are non-temporal (the
-  // 8B-class full model at batch 1: 4.32 -> 4.27 ms per denoise step over a
-  // 1024-position prefix, 4.49 -> 4.31 over 4096; for the LM head and the
-  // batch-32 tiles, which reuse weight tiles across row tiles, it was slower).
-  constexpr bool NT_W = EPI == EPI_SPLITK && BM <= 64;
+  // Products of short row counts (one canvas at batch 1-2: the split layer
+  // projections and the LM head) read every weight exactly once: those weight
+  // loads are non-temporal, which keeps them from pushing out data the rest of
+  // the step reuses (8B-class full model at batch 1: 4.32 -> 4.27 ms per denoise
+  // step over a 1024-position prefix, 4.49 -> 4.31 over 4096, for the split
+  // projections; 0.193 -> 0.165 ms for the head).  Only with 64-deep stages: a
+  // 32-deep stage reads half of each 128-byte weight line, and an early-evicted
+  // line is fetched again for the other half (the head took 0.266 ms).  The
+  // batch-32 tiles reuse weight tiles across row tiles and keep normal loads.
+  constexpr bool NT_W = (EPI == EPI_SPLITK || EPI == EPI_HEAD) && BM <= 64 && BK == 64;
   auto issue = [&](int kt) {  // kt counts this workgroup's stages from 0
     uint8_t* dst = lds + (kt % NBUF) * STAGE + w * BLK * 1024;
 #pragma unroll
@@ -547,7 +551,9 @@ static hipError_t launch_epi(const GemmArgs& g, hipStream_t s) {
     // split evenly are both launched, and only the one needing fewer row tiles
     // runs (e.g. 530 rows: two tiles of 288 rows instead of three).
     if (g.M <= 64) {
-      launch_tiled<EPI, 256, 64, 4, 1, 4>(g, s);  // 4 stages: 194 vs 202 us with 3 (6: 212)
+      // 64-deep stages, two buffers, non-temporal weights: 165 us (32-deep stages
+      // with normal loads: 193 us with 4 buffers, 202 with 3, 212 with 6)
+      launch_tiled<EPI, 256, 64, 4, 1, 2, 64>(g, s);
     } else if (g.M <= 128) {
       launch_tiled<EPI, 256, 128, 4, 2, 3>(g, s);
     } else {
