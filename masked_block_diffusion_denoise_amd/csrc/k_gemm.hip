@@ -500,6 +500,13 @@ static bool long_k_split(int M, int N, int K) {
 
 static int tiles128(int M, int N) { return (N / 128) * ((M + 127) / 128); }
 
+// Short products with many weight rows (the SwiGLU gate/up at batch 1: 28672)
+// stream through 256 x 64 tiles with 64-deep stages, two buffers and
+// non-temporal weights, the LM head's short tile, K split for about 512
+// workgroups: gate/up at 32 rows 51 -> 48 us, at one row 45 -> 40 us; the
+// 8B-class full-model batch-1 step 4.17 -> 4.07 ms.
+static bool short_wide(int N) { return N % 256 == 0 && N / SK_BN >= 128; }
+
 int gemm_ksplit(int M, int N, int K) {
   if (long_k_split(M, N, K)) {
     const int tiles = (N / 256) * ((M + 255) / 256);
@@ -509,6 +516,10 @@ int gemm_ksplit(int M, int N, int K) {
     const int t = tiles128(M, N);
     if (t >= FEW_TILES) return 1;
     return std::max(1, std::min({(256 + t - 1) / t, K / (8 * 64), SPLIT_MAX}));
+  }
+  if (short_wide(N)) {
+    const int t = N / 256;
+    return std::max(1, std::min({(512 + t - 1) / t, K / (16 * 64), SPLIT_MAX}));
   }
   const int tiles = N / SK_BN;
   const int want = (640 + tiles - 1) / tiles;
@@ -536,6 +547,8 @@ static void launch_partials(const GemmArgs& h, hipStream_t s) {
     launch_tiled<EPI_SPLITK, 256, 256, 4, 2, 2, 64>(h, s);
   else if (h.M > SK_BM)
     launch_tiled<EPI_SPLITK, 128, 128, 2, 2, 3, 64>(h, s);
+  else if (short_wide(h.N))
+    launch_tiled<EPI_SPLITK, 256, 64, 4, 1, 2, 64>(h, s);
   else
     launch_tiled<EPI_SPLITK, SK_BN, SK_BM, 4, 1, 3, 64>(h, s);
 }

@@ -1,6 +1,7 @@
 """bf16 MFMA GEMM epilogues vs float64 products of the same bf16 values.
 
-Shapes cover the skinny path (M <= 64, with and without split-K), the tiled path
+Shapes cover the skinny paths (M <= 64, with and without split-K, 128- and
+256-wide weight tiles), the tiled path
 (M > 64, ragged last row tile) and the 8B-class projection sizes.
 """
 import numpy as np
@@ -18,7 +19,9 @@ SHAPES = [(16, 256, 128), (13, 1024, 512), (32, 6144, 4096), (64, 384, 256), (32
           (128, 256, 128), (200, 384, 512), (1024, 512, 4096), (96, 1024, 1024),
           # the tiny model's projections (K parts of one or no 32-deep step per wavefront)
           (32, 256, 128), (32, 128, 128), (32, 128, 512), (64, 256, 128), (48, 128, 512), (2, 1024, 128),
-          (80, 256, 128)]
+          (80, 256, 128),
+          # short and wide: 256 x 64 tiles, K split (ragged rows)
+          (20, 32768, 2048)]
 
 
 def operands(M, N, K, seed):
