@@ -11,10 +11,11 @@
 // tiles, 32- or 64-deep K stages in a ring of LDS buffers filled by direct
 // global-to-LDS loads, each wavefront a block of v_mfma_f32_32x32x16_bf16
 // tiles.  Short products (one canvas at batch 1-2) are HBM-bound: their
-// activation rows are loaded once per workgroup and shared from LDS, and when
-// there are too few weight tiles to fill the chip K is split over workgroups,
-// the fp32 partials summed in a fixed order by a second kernel or by the
-// caller's next step (no cross-workgroup atomics or fences).
+// activation rows are loaded once per workgroup and shared from LDS, their
+// weights (read once) with non-temporal loads, and when there are too few
+// weight tiles to fill the chip K is split over workgroups, the fp32 partials
+// summed in a fixed order by a second kernel or by the caller's next step (no
+// cross-workgroup atomics or fences).
 #include <algorithm>
 
 #include "dlm_device.h"
@@ -479,11 +480,11 @@ __global__ void __launch_bounds__(256) k_splitk_reduce(GemmArgs g) {
 int gemm_head_tile_n(int) { return 256; }
 
 // Short products (M <= 64 rows: one canvas at batch 1-2) stream their weights
-// once through 128 x 64 tiles.  With too few weight tiles to fill the chip, K is
-// split so that several hundred workgroups stream disjoint weight slices; each
-// K range stays at least 16 stages deep and at most 8 splits are made, since
-// every split adds an fp32 partial plane to write and reduce (measured best:
-// 3 splits for 224 tiles, 8 for 32-48 tiles).
+// once through 128 x 64 tiles (256 x 64 with many weight rows, below).  With
+// too few weight tiles to fill the chip, K is split so that several hundred
+// workgroups stream disjoint weight slices; each K range stays at least 16
+// stages deep and at most 8 splits are made, since every split adds an fp32
+// partial plane to write and reduce (measured best: 8 splits for 32-48 tiles).
 constexpr int SK_BN = 128, SK_BM = 64;
 
 // Long-K products with few 256 x 256 tiles (the down projection at batch 32:
