@@ -464,14 +464,16 @@ static hipError_t launch(const AttnArgs& a, hipStream_t s) {
   const int splits = attn_splits(a, &chunk);
   const int qblocks = (a.Lq + 31) / 32;
   dim3 grid(splits, qblocks, a.B * a.G);
-  // K/V of this launch larger than the 256 MB last-level cache (e.g. batch 4
-  // over 65536 positions: 1 GB) stream non-temporally and leave the cached
-  // data of the rest of the step alone (8B-class full model, batch 4 over 65536
-  // positions: 12.25 -> 11.79 ms per denoise step).  Smaller K/V stay cacheable:
-  // the denoise steps of a block read the same prefix again (batch 1 over 4096
-  // positions was slower with non-temporal loads).
+  // Large K/V streams of one launch (over 64 MB, a quarter of the 256 MB
+  // last-level cache: their layers' K/V together cannot stay cached from one
+  // denoise step to the next) load non-temporally and leave the cached data of
+  // the rest of the step alone.  8B-class full model: batch 4 over 65536
+  // positions (1 GB per layer) 12.25 -> 11.79 ms per denoise step, batch 32
+  // over ~1100 (150 MB) 19.04 -> 18.93 ms.  Small K/V stay cacheable: the
+  // denoise steps of a block re-read the same prefix (batch 1 over 4096
+  // positions, 17 MB, was slower with non-temporal loads).
   const double kv_bytes = 2.0 * a.B * a.G * static_cast<double>(a.max_kv) * HD * 2;
-  if (kv_bytes > 256.0 * (1 << 20))
+  if (kv_bytes > 64.0 * (1 << 20))
     hipLaunchKernelGGL((k_attn<HD, GS, true>), grid, dim3(GS * 64), 0, s, a, chunk);
   else
     hipLaunchKernelGGL((k_attn<HD, GS, false>), grid, dim3(GS * 64), 0, s, a, chunk);
