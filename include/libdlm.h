@@ -60,6 +60,7 @@ typedef enum {
  * head_dim in {32, 128}; n_heads / n_kv_heads in {1, 2, 4}; d_model,
  * n_heads*head_dim and d_ffn multiples of 256 (or 64..256 and multiples of 64);
  * (n_heads + 2*n_kv_heads)*head_dim, d_model and 2*d_ffn multiples of 128;
+ * d_model <= 8192;
  * vocab a multiple of 256; 0 <= mask_id < vocab; rope_base > 0; rms_eps > 0. */
 typedef struct {
   int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, d_ffn, vocab, mask_id;

@@ -401,6 +401,8 @@ dlm_status dlm_model_create(const dlm_config* cfg, const dlm_weights* w, dlm_mod
     return fail(DLM_ERR_UNSUPPORTED, "d_model, n_heads*head_dim and d_ffn must be multiples of 256 (or of 64 up to 256)");
   if (qkv_dim(c) % 128 || c.d_model % 128 || (2 * c.d_ffn) % 128 || c.vocab % 256)
     return fail(DLM_ERR_UNSUPPORTED, "(H+2G)*hd, d_model and 2*d_ffn must be multiples of 128, vocab of 256");
+  if (c.d_model > 8192)  // the row kernels (embedding, residual + norm) run one thread per 8 columns
+    return fail(DLM_ERR_UNSUPPORTED, "d_model %d > 8192", c.d_model);
   if (c.mask_id < 0 || c.mask_id >= c.vocab) return fail(DLM_ERR_INVALID_ARG, "mask_id %d outside [0, %d)", c.mask_id, c.vocab);
   if (!(std::isfinite(c.rope_base) && c.rope_base > 0.f)) return fail(DLM_ERR_INVALID_ARG, "rope_base must be finite and > 0");
   if (!(std::isfinite(c.rms_eps) && c.rms_eps > 0.f)) return fail(DLM_ERR_INVALID_ARG, "rms_eps must be finite and > 0");

@@ -46,9 +46,17 @@ __global__ void __launch_bounds__(256) k_commit(const float* __restrict__ conf,
   if (b >= B) return;  // uniform per wavefront
   const size_t base = static_cast<size_t>(b) * L;
   const bool in = lane < L;
+  // every input is loaded before any is used (one memory round trip)
   const bool mk = in && masked[base + lane] != 0;
   const float c = in ? conf[base + lane] : 0.f;
   const float e = (in && entropy) ? entropy[base + lane] : 0.f;
+  const int st = steps[b];
+  const int a = in ? argmax[base + lane] : 0;
+  const float tb = tau[b];
+  const int qb = quota[b];
+  const bool adaptive = o.stability_steps > 0;
+  const int prev = (adaptive && in) ? o.prev_argmax[base + lane] : 0;
+  const int stable_in = adaptive ? o.stable[b] : 0;
   const unsigned long long mball = __ballot(mk);
   const int cnt = __popcll(mball);
   if (cnt == 0) {
@@ -58,13 +66,11 @@ __global__ void __launch_bounds__(256) k_commit(const float* __restrict__ conf,
     }
     return;
   }
-  const int st = steps[b];
-  const int a = in ? argmax[base + lane] : 0;
 
   bool stop = false;
-  if (o.stability_steps > 0) {
-    const bool diff = mk && a != o.prev_argmax[base + lane];
-    const int stable = __any(diff) ? 0 : o.stable[b] + 1;
+  if (adaptive) {
+    const bool diff = mk && a != prev;
+    const int stable = __any(diff) ? 0 : stable_in + 1;
     float total = 0.f;  // sequential, in position order
     for (int i = 0; i < L; ++i) {
       const float ei = __shfl(e, i, WAVE);
@@ -92,7 +98,7 @@ __global__ void __launch_bounds__(256) k_commit(const float* __restrict__ conf,
   } else {
     bool inA;
     if (o.rule == COMMIT_BOUND) {
-      inA = mk && (c >= tau[b] || (c >= o.min_threshold && c >= 1.f - o.scaling / static_cast<float>(lane + 2)));
+      inA = mk && (c >= tb || (c >= o.min_threshold && c >= 1.f - o.scaling / static_cast<float>(lane + 2)));
     } else if (o.rule == COMMIT_ENTROPY) {
       // running sum of the entropies in rank order (float32, sequential)
       float total = 0.f, mine = 0.f;
@@ -103,11 +109,11 @@ __global__ void __launch_bounds__(256) k_commit(const float* __restrict__ conf,
       }
       inA = mk && mine <= o.entropy_bound;
     } else {
-      inA = mk && c > tau[b];
+      inA = mk && c > tb;
     }
     const unsigned long long aball = __ballot(inA);
     const int nA = __popcll(aball);
-    const int q = min(quota[b], cnt);
+    const int q = min(qb, cnt);
     if (nA >= q) {
       chosen = inA;
       n = nA;
@@ -165,6 +171,19 @@ __device__ __forceinline__ float block_sum_256(float v, float* red) {
   return t;
 }
 
+// Sum over a workgroup of T threads (wave sums, then the waves in order).
+template <int T>
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int i = 0; i < T / 64; ++i) t += red[i];
+  return t;
+}
+
 __device__ __forceinline__ void unpack8(u32x4 v, float* f) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -199,56 +218,65 @@ __device__ __forceinline__ void rope_entry(const RopeSpec& r, int e) {
 // RMSNorm being x / sqrt(mean(x^2) + eps) * g; out-of-range tokens read as
 // zeros and are counted.  Blocks past M fill the RoPE table of the pass (one
 // launch for both).
-__global__ void __launch_bounds__(256) k_embed_norm(const int* __restrict__ tokens, int M, int Lq, int tok_ld,
-                                                    const bf16_t* __restrict__ E, int V, int d,
-                                                    const bf16_t* __restrict__ g, float eps,
-                                                    float* __restrict__ x, bf16_t* __restrict__ xn,
-                                                    int* __restrict__ bad, RopeSpec rope) {
-  __shared__ float red[4];
+template <int T>
+__global__ void __launch_bounds__(T) k_embed_norm(const int* __restrict__ tokens, int M, int Lq, int tok_ld,
+                                                  const bf16_t* __restrict__ E, int V, int d,
+                                                  const bf16_t* __restrict__ g, float eps,
+                                                  float* __restrict__ x, bf16_t* __restrict__ xn,
+                                                  int* __restrict__ bad, RopeSpec rope) {
+  __shared__ float red[T / 64];
   const int m = blockIdx.x;
   if (m >= M) {
-    const int e = (m - M) * 256 + threadIdx.x;
+    const int e = (m - M) * T + threadIdx.x;
     if (e < rope.total) rope_entry(rope, e);
     return;
   }
+  // one thread per 8 columns: the row stays in registers for the normalisation
+  const int c = threadIdx.x;
+  const bool on = c < d / 8;
   const int t = tokens[static_cast<size_t>(m / Lq) * tok_ld + m % Lq];
   const bool ok = t >= 0 && t < V;
   if (!ok && threadIdx.x == 0 && bad) atomicAdd(bad, 1);
   const bf16_t* row = E + static_cast<size_t>(ok ? t : 0) * d;
+  float f[8], gg[8];
   float ss = 0.f;
-  for (int c = threadIdx.x; c < d / 8; c += 256) {
-    float f[8];
-    u32x4 v = ok ? ld16(row + c * 8) : u32x4{0, 0, 0, 0};
-    unpack8(v, f);
-    float* xo = x + static_cast<size_t>(m) * d + c * 8;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      xo[i] = f[i];
-      ss += f[i] * f[i];
-    }
-  }
-  const float rstd = rsqrtf(block_sum_256(ss, red) / d + eps);
-  for (int c = threadIdx.x; c < d / 8; c += 256) {
-    float f[8], gg[8];
-    u32x4 v = ok ? ld16(row + c * 8) : u32x4{0, 0, 0, 0};
-    unpack8(v, f);
+  if (on) {
+    unpack8(ok ? ld16(row + c * 8) : u32x4{0, 0, 0, 0}, f);
     unpack8(ld16(g + c * 8), gg);
-    u32x4 o;
+    float* xo = x + static_cast<size_t>(m) * d + c * 8;
+    *reinterpret_cast<float4*>(xo) = make_float4(f[0], f[1], f[2], f[3]);
+    *reinterpret_cast<float4*>(xo + 4) = make_float4(f[4], f[5], f[6], f[7]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(f[2 * i] * rstd * gg[2 * i], f[2 * i + 1] * rstd * gg[2 * i + 1]);
-    st16(xn + static_cast<size_t>(m) * d + c * 8, o);
+    for (int i = 0; i < 8; ++i) ss += f[i] * f[i];
   }
+  const float rstd = rsqrtf(block_sum<T>(ss, red) / d + eps);
+  if (!on) return;
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(f[2 * i] * rstd * gg[2 * i], f[2 * i + 1] * rstd * gg[2 * i + 1]);
+  st16(xn + static_cast<size_t>(m) * d + c * 8, o);
 }
 
 hipError_t embed_norm(const int* tokens, int M, int Lq, int tok_ld, const void* embed, int V, int d,
                       const void* gain, float eps, float* x, void* xn, int* bad_token, const int* prefix,
                       int pos_offset, int hd, float base, float2* tab, hipStream_t s) {
   if (M <= 0) return hipSuccess;
+  if (d % 8 || d / 8 > 1024) return hipErrorInvalidValue;
   RopeSpec r{prefix, pos_offset, Lq, hd / 2, log(static_cast<double>(base)), tab, tab ? M * (hd / 2) : 0};
-  const int tab_blocks = (r.total + 255) / 256;
-  hipLaunchKernelGGL(k_embed_norm, dim3(M + tab_blocks), dim3(256), 0, s, tokens, M, Lq, tok_ld,
-                     static_cast<const bf16_t*>(embed), V, d, static_cast<const bf16_t*>(gain), eps, x,
-                     static_cast<bf16_t*>(xn), bad_token, r);
+  auto go = [&](auto kern, int T) {
+    hipLaunchKernelGGL(kern, dim3(M + (r.total + T - 1) / T), dim3(T), 0, s, tokens, M, Lq, tok_ld,
+                       static_cast<const bf16_t*>(embed), V, d, static_cast<const bf16_t*>(gain), eps, x,
+                       static_cast<bf16_t*>(xn), bad_token, r);
+  };
+  const int need = d / 8;
+  if (need <= 64)
+    go(k_embed_norm<64>, 64);
+  else if (need <= 256)
+    go(k_embed_norm<256>, 256);
+  else if (need <= 512)
+    go(k_embed_norm<512>, 512);
+  else
+    go(k_embed_norm<1024>, 1024);
   return hipGetLastError();
 }
 
@@ -280,19 +308,6 @@ __global__ void __launch_bounds__(256) k_rmsnorm(const float* __restrict__ x, in
     o[3] = pack_bf16x2(v1.z * rstd * gg[6], v1.w * rstd * gg[7]);
     st16(xn + static_cast<size_t>(i) * d + c * 8, o);
   }
-}
-
-// Sum over a workgroup of T threads (wave sums, then the waves in order).
-template <int T>
-__device__ __forceinline__ float block_sum(float v, float* red) {
-  v = wave_sum(v);
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) red[w] = v;
-  __syncthreads();
-  float t = 0.f;
-#pragma unroll
-  for (int i = 0; i < T / 64; ++i) t += red[i];
-  return t;
 }
 
 // Residual update from K-split partials fused with the next RMSNorm:

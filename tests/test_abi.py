@@ -59,7 +59,7 @@ def create(cfg):
     (dict(head_dim=64), -4), (dict(n_heads=3), -2), (dict(n_heads=16, n_kv_heads=2), -4),
     (dict(mask_id=1024), -1), (dict(mask_id=-1), -1), (dict(vocab=1000), -4), (dict(vocab=1152), -4),
     (dict(d_ffn=500), -4), (dict(rope_base=float("nan")), -1), (dict(rms_eps=0.0), -1),
-    (dict(n_layers=0), -2),
+    (dict(n_layers=0), -2), (dict(d_model=8448), -4),
 ])
 def test_model_create_rejects_bad_config(kw, status):
     st, _ = create(tiny_cfg(**kw))
