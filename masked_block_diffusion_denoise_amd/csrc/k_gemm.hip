@@ -590,14 +590,18 @@ static hipError_t launch_epi(const GemmArgs& g, hipStream_t s) {
     launch_tiled<EPI, SK_BN, SK_BM, 4, 1, 3, 64>(g, s);
   } else {
     // 256 x 256 tiles where they still give at least one wave of workgroups
-    // (the SwiGLU gate/up projection); 128 x 128 otherwise: with at most one
-    // tile per CU (down, O projections at batch 32) one workgroup per CU with a
-    // deeper ring of 64-deep stages, else two per CU with 32-deep stages
+    // (the SwiGLU gate/up projection); else with at most one 128 x 128 tile per
+    // CU (down, O projections at batch 32) one workgroup per CU with a deeper
+    // ring of 64-deep stages; else 256 x 128 tiles, two per CU with 32-deep
+    // stages (QKV at batch 32: 95 -> 84 us against 128 x 128 tiles, which move
+    // a third more bytes per flop)
     const int t128 = (g.N / 128) * ((g.M + 127) / 128);
     if (g.N % 256 == 0 && (g.N / 256) * ((g.M + 255) / 256) >= 256)
       launch_tiled<EPI, 256, 256, 4, 2, 2, 64>(g, s);
     else if (t128 <= 256)
       launch_tiled<EPI, 128, 128, 2, 2, 3, 64>(g, s);
+    else if (g.N % 256 == 0)
+      launch_tiled<EPI, 256, 128, 4, 2, 3>(g, s);
     else
       launch_tiled<EPI, 128, 128, 2, 2, 4>(g, s);
   }
