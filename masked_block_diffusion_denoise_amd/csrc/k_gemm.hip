@@ -598,7 +598,9 @@ static hipError_t launch_epi(const GemmArgs& g, hipStream_t s) {
     const int t128 = (g.N / 128) * ((g.M + 127) / 128);
     if (g.N % 256 == 0 && (g.N / 256) * ((g.M + 255) / 256) >= 256)
       launch_tiled<EPI, 256, 256, 4, 2, 2, 64>(g, s);
-    else if (t128 <= 256)
+    else if (t128 <= 256 && g.M > 128)  // several row tiles: MFMA-bound (O at 1024 rows 55 -> 52 us)
+      launch_tiled<EPI, 128, 128, 2, 2, 2, 64>(g, s);
+    else if (t128 <= 256)  // one row tile: HBM-bound, deeper ring (gate/up at 128 rows: 58 vs 74 us)
       launch_tiled<EPI, 128, 128, 2, 2, 3, 64>(g, s);
     else if (g.N % 256 == 0)
       launch_tiled<EPI, 256, 128, 4, 2, 3>(g, s);

@@ -23,7 +23,9 @@ SHAPES = [(16, 256, 128), (13, 1024, 512), (32, 6144, 4096), (64, 384, 256), (32
           # short and wide: 256 x 64 tiles, K split (ragged rows)
           (20, 32768, 2048),
           # more than one 128 x 128 tile per CU but too few 256 x 256 tiles: 256 x 128 (ragged rows)
-          (1000, 4608, 256)]
+          (1000, 4608, 256),
+          # at most one 128 x 128 tile per CU, several row tiles (ragged rows)
+          (1000, 2048, 256)]
 
 
 def operands(M, N, K, seed):
