@@ -27,9 +27,10 @@ def test_rmsnorm(M, d):
 
 
 @pytest.mark.parametrize("H,G,hd,base", [(4, 2, 32, 1e4), (32, 8, 128, 1e6)])
-def test_rope_kv_write(H, G, hd, base):
-    announce(f"rope H={H} G={G} hd={hd}")
-    B, Lq, cap = 3, 32, 70144
+@pytest.mark.parametrize("Lq", [32, 13])  # 13: groups of 16 rows span two batch rows
+def test_rope_kv_write(H, G, hd, base, Lq):
+    announce(f"rope H={H} G={G} hd={hd} Lq={Lq}")
+    B, cap = 3, 70144
     prefix = np.array([0, 100, 70000], dtype=np.int32)
     off = 5
     nh = H + 2 * G
