@@ -152,3 +152,37 @@ def test_dense8b_linear_spec_accounting(dense8b):
     ar = host(R.Session(dense8b, 1, T + n_new + 64, 1).generate_ar(prompt, n_new))[0]
     assert toks[0] == ar[0]  # both take the prefill's causal argmax
     torch.cuda.empty_cache()
+
+
+def test_dense8b_decode_is_deterministic(dense8b):
+    """Every reduction on the path sums in a fixed order (K-split partials in split
+    order, attention splits in split order, vocabulary tiles of the head in tile
+    order): the same prompt decoded twice gives bit-identical confidences, tokens
+    and KV caches.  Batch 2 over a short prompt takes the split projections, the
+    split attention with its merge and the head merge."""
+    announce("dense8b determinism")
+    B, T, Lb, max_steps = 2, 600, 32, 4  # 632 keys: two attention splits of >= 256 keys
+    prompt = synth.prompt(SHAPE, B, T, seed=21)
+    tau = torch.full((B,), 0.9, dtype=torch.float32, device="cuda")
+    quota = torch.ones(B, dtype=torch.int32, device="cuda")
+    runs = []
+    for _ in range(2):
+        sess = R.Session(dense8b, B, 704, Lb)
+        sess.prefill(i32(prompt))
+        confs = []
+        sess.begin_block()
+        for _ in range(max_steps):
+            sess.denoise_step()
+            confs.append(host(sess.conf).copy())
+            sess.commit(tau, quota, max_steps)
+        sess.append_block()
+        sync()
+        k, v = host(sess.kv.k_logical()[:, :, :, :T + Lb]), host(sess.kv.v_logical()[:, :, :, :T + Lb])
+        runs.append((np.stack(confs), host(sess.canvas).copy(), k, v))
+        del sess
+    (c0, t0, k0, v0), (c1, t1, k1, v1) = runs
+    np.testing.assert_array_equal(c1, c0)
+    np.testing.assert_array_equal(t1, t0)
+    np.testing.assert_array_equal(k1, k0)
+    np.testing.assert_array_equal(v1, v0)
+    assert (t0 != MASK).all()
