@@ -51,8 +51,8 @@ __device__ __forceinline__ uint32_t att_lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p));
 }
 
-// NT: cache policy non-temporal (evicted first), for K/V streams larger than
-// the last-level cache
+// NT: cache policy non-temporal (evicted first), for large K/V streams (the
+// launch picks it above 64 MB per launch)
 template <bool NT>
 __device__ __forceinline__ void att_load_lds16(const void* src, void* lds_dst) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 16, 0, NT ? 2 : 0);
