@@ -190,9 +190,25 @@ __device__ __forceinline__ void lds_frags_1_2(uint32_t a, uint32_t b, u32x4 (&fa
       : "memory");
 }
 
+template <int D>
+__device__ __forceinline__ void lds_frags_3_2(uint32_t a, uint32_t b, u32x4 (&fa)[3], u32x4 (&fb)[2]) {
+  asm volatile(
+      "ds_read_b128 %0, %5\n\t"
+      "ds_read_b128 %1, %5 offset:%7\n\t"
+      "ds_read_b128 %2, %5 offset:%8\n\t"
+      "ds_read_b128 %3, %6\n\t"
+      "ds_read_b128 %4, %6 offset:%7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(fa[0]), "=&v"(fa[1]), "=&v"(fa[2]), "=&v"(fb[0]), "=&v"(fb[1])
+      : "v"(a), "v"(b), "i"(D), "i"(2 * D)
+      : "memory");
+}
+
 template <int TN, int TM, int D>
 __device__ __forceinline__ void lds_frags(uint32_t a, uint32_t b, u32x4 (&fa)[TN], u32x4 (&fb)[TM]) {
-  if constexpr (TN == 2 && TM == 4)
+  if constexpr (TN == 3 && TM == 2)
+    lds_frags_3_2<D>(a, b, fa, fb);
+  else if constexpr (TN == 2 && TM == 4)
     lds_frags_2_4<D>(a, b, fa, fb);
   else if constexpr (TN == 2 && TM == 5)
     lds_frags_2_5<D>(a, b, fa, fb);
@@ -592,9 +608,10 @@ static hipError_t launch_epi(const GemmArgs& g, hipStream_t s) {
     // 256 x 256 tiles where they still give at least one wave of workgroups
     // (the SwiGLU gate/up projection); else with at most one 128 x 128 tile per
     // CU (down, O projections at batch 32) one workgroup per CU with a deeper
-    // ring of 64-deep stages; else 256 x 128 tiles, two per CU with 32-deep
-    // stages (QKV at batch 32: 95 -> 84 us against 128 x 128 tiles, which move
-    // a third more bytes per flop)
+    // ring of 64-deep stages; else 192 x 128 tiles where they come to at most
+    // one per CU (QKV at batch 32: 6144 / 192 x 8 = 256 tiles, 80 -> 68 us
+    // against two 256 x 128 tiles per CU); else 256 x 128 tiles, two per CU
+    // with 32-deep stages (a third fewer bytes per flop than 128 x 128)
     const int t128 = (g.N / 128) * ((g.M + 127) / 128);
     if (g.N % 256 == 0 && (g.N / 256) * ((g.M + 255) / 256) >= 256)
       launch_tiled<EPI, 256, 256, 4, 2, 2, 64>(g, s);
@@ -602,6 +619,8 @@ static hipError_t launch_epi(const GemmArgs& g, hipStream_t s) {
       launch_tiled<EPI, 128, 128, 2, 2, 2, 64>(g, s);
     else if (t128 <= 256)  // one row tile: HBM-bound, deeper ring (gate/up at 128 rows: 58 vs 74 us)
       launch_tiled<EPI, 128, 128, 2, 2, 3, 64>(g, s);
+    else if (g.N % 192 == 0 && (g.N / 192) * ((g.M + 127) / 128) <= 256)
+      launch_tiled<EPI, 192, 128, 2, 2, 2, 64>(g, s);
     else if (g.N % 256 == 0)
       launch_tiled<EPI, 256, 128, 4, 2, 3>(g, s);
     else

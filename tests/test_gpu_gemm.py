@@ -1,8 +1,8 @@
 """bf16 MFMA GEMM epilogues vs float64 products of the same bf16 values.
 
 Shapes cover the skinny paths (M <= 64, with and without split-K, 128- and
-256-wide weight tiles), the tiled path
-(M > 64, ragged last row tile) and the 8B-class projection sizes.
+256-wide weight tiles), each tile shape of the tiled path (M > 64, ragged last
+row tile) and the 8B-class projection sizes.
 """
 import numpy as np
 import pytest
@@ -22,8 +22,12 @@ SHAPES = [(16, 256, 128), (13, 1024, 512), (32, 6144, 4096), (64, 384, 256), (32
           (80, 256, 128),
           # short and wide: 256 x 64 tiles, K split (ragged rows)
           (20, 32768, 2048),
-          # more than one 128 x 128 tile per CU but too few 256 x 256 tiles: 256 x 128 (ragged rows)
-          (1000, 4608, 256),
+          # more than one 128 x 128 tile per CU, at most one 192 x 128 tile per CU (ragged rows),
+          # and the QKV projection of the 8B-class model at batch 32
+          (1000, 4608, 256), (1024, 6144, 4096),
+          # more than one 128 x 128 or 192 x 128 tile per CU, too few 256 x 256 tiles:
+          # 256 x 128 (ragged rows)
+          (1000, 5120, 256),
           # at most one 128 x 128 tile per CU, several row tiles (ragged rows)
           (1000, 2048, 256)]
 
@@ -67,7 +71,8 @@ def test_gemm_residual_f32(M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(16, 1024, 128), (32, 28672, 4096), (40, 512, 256), (160, 1024, 512),
-                                   (1024, 2048, 4096), (32, 1024, 128), (64, 1024, 128), (80, 1024, 128)])
+                                   (1024, 2048, 4096), (32, 1024, 128), (64, 1024, 128), (80, 1024, 128),
+                                   (1000, 4608, 256)])
 def test_gemm_swiglu(M, N, K):
     announce(f"gemm swiglu {M}x{N}x{K}")
     a, w = operands(M, N, K, 3)
