@@ -29,7 +29,11 @@ SHAPES = [(16, 256, 128), (13, 1024, 512), (32, 6144, 4096), (64, 384, 256), (32
           # 256 x 128 (ragged rows)
           (1000, 5120, 256),
           # at most one 128 x 128 tile per CU, several row tiles (ragged rows)
-          (1000, 2048, 256)]
+          (1000, 2048, 256),
+          # at least one 256 x 256 tile per CU: one 64-deep stage, two (ragged rows)
+          (520, 32768, 64), (520, 32768, 128),
+          # long K over few 256 x 256 tiles: K split into 8 parts of 16 stages
+          (300, 1024, 8192)]
 
 
 def operands(M, N, K, seed):
@@ -72,7 +76,7 @@ def test_gemm_residual_f32(M, N, K):
 
 @pytest.mark.parametrize("M,N,K", [(16, 1024, 128), (32, 28672, 4096), (40, 512, 256), (160, 1024, 512),
                                    (1024, 2048, 4096), (32, 1024, 128), (64, 1024, 128), (80, 1024, 128),
-                                   (1000, 4608, 256)])
+                                   (1000, 4608, 256), (520, 32768, 128)])
 def test_gemm_swiglu(M, N, K):
     announce(f"gemm swiglu {M}x{N}x{K}")
     a, w = operands(M, N, K, 3)
