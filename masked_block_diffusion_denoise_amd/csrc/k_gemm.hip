@@ -25,32 +25,6 @@ namespace dlm {
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
-// Reduce four logits of columns n0..n0+3 (one row) to a (max, sum exp, argmax) partial.
-__device__ __forceinline__ MaxSumIdx head_quad(const float* v, int n0, int mask_id, bool& bad) {
-  float x[4];
-  MaxSumIdx r{-INFINITY, 0.f, 0x7fffffff, 0.f};
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    x[u] = v[u];
-    if (n0 + u == mask_id) x[u] = -INFINITY;
-    else if (!__builtin_isfinite(x[u])) bad = true;
-    if (x[u] > r.m) {
-      r.m = x[u];
-      r.idx = n0 + u;
-    }
-  }
-  if (r.m != -INFINITY) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (x[u] != -INFINITY) {  // the mask id adds nothing (0 * -inf would be NaN)
-        const float e = __expf(x[u] - r.m);
-        r.s += e;
-        r.t += e * (x[u] - r.m);
-      }
-  }
-  return r;
-}
-
 __device__ __forceinline__ MaxSumIdx msi_shfl_xor(MaxSumIdx a, int mask) {
   MaxSumIdx b;
   b.m = __shfl_xor(a.m, mask, WAVE);
@@ -424,24 +398,58 @@ __global__ void __launch_bounds__(WN * WM * 64) k_gemm_tiled(GemmArgs g) {
     float* rs = rm + WN * BM;
     float* rt = rs + WN * BM;
     int* ri = reinterpret_cast<int*>(rt + WN * BM);
+    // Per row, two passes over the lane's TN x 16 logits: their max, then the
+    // sums of exp2((x - max) log2 e) and of that times (x - max) log2 e, and the
+    // lowest column holding the max.  The mask id's column (in at most one tile
+    // of the vocabulary) is pinned to -1e30 first, so that it adds exactly
+    // nothing and never holds the max.  A non-finite logit makes a sum NaN
+    // (NaN and +inf through the exponential, -inf through 0 x -inf), which is
+    // what flags the row.  Register r of fragment i holds column
+    // nb + 32 i + 8 (r / 4) + r % 4.
+    constexpr float LOG2E = 1.4426950408889634f, LN2 = 0.6931471805599453f;
+    const int nb = n0 + wn * TN * 32 + 4 * ahalf;
+    const bool mask_here = g.mask_id >= n0 && g.mask_id < n0 + BN;
     bool bad = false;
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
       const int ml = (wm * TM + j) * 32 + arow, m = m0 + ml;
-      MaxSumIdx p{-INFINITY, 0.f, 0x7fffffff, 0.f};
+      if (g.logits && m < M) {
 #pragma unroll
-      for (int i = 0; i < TN; ++i)
+        for (int i = 0; i < TN; ++i)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n = n0 + (wn * TN + i) * 32 + 8 * q + 4 * ahalf;
-          float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-          if (g.logits && m < M) {
-            float4 o4 = make_float4(v[0], v[1], v[2], v[3]);
+          for (int q = 0; q < 4; ++q) {
+            const int n = nb + 32 * i + 8 * q;
+            float4 o4 = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
             if (n <= g.mask_id && g.mask_id < n + 4) (&o4.x)[g.mask_id - n] = -INFINITY;
             *reinterpret_cast<float4*>(g.logits + static_cast<size_t>(g.logit_rows ? g.logit_rows[m] : m) * g.N + n) = o4;
           }
-          p = msi_combine(p, head_quad(v, n, g.mask_id, bad));
+      }
+      if (mask_here) {
+#pragma unroll
+        for (int i = 0; i < TN; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (nb + 32 * i + 8 * (r / 4) + r % 4 == g.mask_id) acc[i][j][r] = -1e30f;
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[i][j][r]);
+      const float m2 = mx * LOG2E;
+      float sum = 0.f, t2 = 0.f;
+      int loc = -1;
+#pragma unroll
+      for (int i = TN - 1; i >= 0; --i)  // columns downwards: the last match is the lowest
+#pragma unroll
+        for (int r = 15; r >= 0; --r) {
+          const float x = acc[i][j][r], d2 = fmaf(x, LOG2E, -m2), e = __builtin_amdgcn_exp2f(d2);
+          sum += e;
+          t2 = fmaf(e, d2, t2);
+          loc = x == mx ? 32 * i + 8 * (r / 4) + r % 4 : loc;
         }
+      bad |= !__builtin_isfinite(sum) || !__builtin_isfinite(t2);
+      MaxSumIdx p{mx, sum, loc < 0 ? 0x7fffffff : nb + loc, t2 * LN2};
       p = msi_shfl_xor(p, 32);
       if (ahalf == 0) {
         rm[wn * BM + ml] = p.m;
