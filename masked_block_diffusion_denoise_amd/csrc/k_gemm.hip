@@ -7,8 +7,8 @@
 // one vector.
 //
 // One tiled kernel for every shape: 256 x 256, 256 x 320 (LM head, rows split
-// evenly on the device), 256 x 128, 256 x 64, 128 x 128 or 128 x 64 output
-// tiles, 32- or 64-deep K stages in a ring of LDS buffers filled by direct
+// evenly on the device), 256 x 128, 192 x 128, 256 x 64, 128 x 128 or 128 x 64
+// output tiles, 32- or 64-deep K stages in a ring of LDS buffers filled by direct
 // global-to-LDS loads, each wavefront a block of v_mfma_f32_32x32x16_bf16
 // tiles.  Short products (one canvas at batch 1-2) are HBM-bound: their
 // activation rows are loaded once per workgroup and shared from LDS, their
