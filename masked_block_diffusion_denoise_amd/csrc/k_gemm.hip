@@ -23,7 +23,11 @@
 
 namespace dlm {
 
-__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
+// g * sigmoid(g) with the hardware reciprocal (1 ulp; the product is stored as
+// bf16) instead of an IEEE division: exp(-g) -> inf for g << 0 gives g * 0.
+__device__ __forceinline__ float silu_f(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.4426950408889634f));
+}
 
 __device__ __forceinline__ MaxSumIdx msi_shfl_xor(MaxSumIdx a, int mask) {
   MaxSumIdx b;
