@@ -190,10 +190,14 @@ size_t layer_kv_elems(const dlm_config& c, const dlm_kv* kv) {
 }
 
 // The decoder stack over B*Lq rows whose query j of row b sits at
-// prefix[b] + pos_offset + j; leaves the final residual stream in p.x.
+// prefix[b] + pos_offset + j; leaves the final residual stream in p.x.  With
+// defer_splits, a K-split last down projection leaves its partials in p.kpart
+// unsummed and *defer_splits = their count (0 when p.x is complete): the caller
+// adds them to the rows it reads.
 dlm_status run_layers(const dlm_model* m, const dlm_kv* kv, const int32_t* tokens, int tok_ld, int B, int Lq,
                       const int32_t* prefix, int pos_offset, int causal, int max_kv, int32_t* flags,
-                      const PassBufs& p, hipStream_t s) {
+                      const PassBufs& p, hipStream_t s, int* defer_splits = nullptr) {
+  if (defer_splits) *defer_splits = 0;
   const dlm_config& c = m->c;
   const int R = B * Lq;
   const int d = c.d_model, qd = c.n_heads * c.head_dim, nq = qkv_dim(c);
@@ -321,8 +325,14 @@ dlm_status run_layers(const dlm_model* m, const dlm_kv* kv, const int32_t* token
     {
       // with the next layer's attention norm (the last layer's final norm is the caller's)
       TimerScope t(DLM_TIMER_DOWN, s, l == 0);
-      if ((st = resid_gemm(g, l + 1 < c.n_layers ? m->attn_norm[l + 1] : nullptr, "gemm down")) != DLM_OK)
+      const int S = gemm_ksplit(g.M, g.N, g.K);
+      if (l + 1 == c.n_layers && defer_splits && S > 1) {
+        DLM_TRY(gemm_partials(g, s), "gemm down");
+        *defer_splits = S;
+      } else if ((st = resid_gemm(g, l + 1 < c.n_layers ? m->attn_norm[l + 1] : nullptr, "gemm down")) !=
+                 DLM_OK) {
         return st;
+      }
     }
   }
   return DLM_OK;
@@ -568,8 +578,13 @@ dlm_status dlm_denoise_step_ex(const dlm_model* m, const dlm_kv* kv, const int32
   if ((st = check_ws(ws, ws_bytes, need)) != DLM_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const PassBufs p = carve(m->c, reinterpret_cast<uintptr_t>(ws), R, B, L, max_kv, false);
-  if ((st = run_layers(m, kv, canvas, L, B, L, prefix_len, 0, 0, max_kv, flags, p, s)) != DLM_OK) return st;
-  DLM_TRY(masked_norm(masked, R, p.x, m->c.d_model, m->final_norm, m->c.rms_eps, p.xn, p.rows, p.count, s),
+  // the last down projection's K-split partials are summed by the final norm,
+  // for the masked rows only
+  int splits = 0;
+  if ((st = run_layers(m, kv, canvas, L, B, L, prefix_len, 0, 0, max_kv, flags, p, s, &splits)) != DLM_OK)
+    return st;
+  DLM_TRY(masked_norm(masked, R, p.x, m->c.d_model, m->final_norm, m->c.rms_eps, p.xn, p.rows, p.count, s, p.kpart,
+                      splits),
           "masked rows + final norm");
   return run_head(m, R, p.rows, p.count, p.rows, conf, argmax, logits, flags, p, s, true, false, entropy);
 }

@@ -109,9 +109,11 @@ hipError_t rope_kv(void* qkv, int M, int Lq, int H, int G, int hd, const float2*
 hipError_t resid_norm(const float* part, int S, int M, float* x, int d, const void* gain, float eps, void* xn,
                       hipStream_t s);
 // rows[0..count) = indices m with masked[m] != 0, ascending, and count[0] = how
-// many, fused with the final RMSNorm of those rows into xn[0..count)
+// many, fused with the final RMSNorm of those rows into xn[0..count).  With
+// S > 0 the rows are x[m] + sum_s part[s][m] (S fp32 partial planes [S][M][d]
+// of the last residual product, summed in split order); x is not written.
 hipError_t masked_norm(const uint8_t* masked, int M, const float* x, int d, const void* gain, float eps, void* xn,
-                       int* rows, int* count, hipStream_t s);
+                       int* rows, int* count, hipStream_t s, const float* part = nullptr, int S = 0);
 // entropy (optional): ln(sum exp) - sum exp*(l - max) / sum exp per row, in nats
 hipError_t head_merge(const void* partials, int n_tiles, int M, const int* rows, const int* m_dev,
                       float* conf, int* argmax, int total_rows, hipStream_t s, float* entropy = nullptr);

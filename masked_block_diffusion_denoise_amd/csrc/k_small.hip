@@ -506,8 +506,11 @@ __global__ void __launch_bounds__(256) k_masked_norm(const uint8_t* __restrict__
                                                      const float* __restrict__ x, int d,
                                                      const bf16_t* __restrict__ g, float eps,
                                                      bf16_t* __restrict__ xn, int* __restrict__ rows,
-                                                     int* __restrict__ count) {
+                                                     int* __restrict__ count, const float* __restrict__ part,
+                                                     int S) {
   __shared__ float red[4];
+  // the row with the partials added (d <= 8192), read back for the normalisation
+  __shared__ float4 sum_row[2048];
   const int m = blockIdx.x;
   float before = 0.f;
   for (int i = threadIdx.x; i < m; i += 256) before += masked[i] ? 1.f : 0.f;
@@ -517,15 +520,34 @@ __global__ void __launch_bounds__(256) k_masked_norm(const uint8_t* __restrict__
   if (!mine) return;
   if (threadIdx.x == 0) rows[idx] = m;
   const float* xr = x + static_cast<size_t>(m) * d;
+  const float4* src = reinterpret_cast<const float4*>(xr);
   float ss = 0.f;
-  for (int c = threadIdx.x; c < d / 4; c += 256) {
-    const float4 v = reinterpret_cast<const float4*>(xr)[c];
-    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  if (S > 0) {
+    const size_t plane = static_cast<size_t>(M) * d;
+    const float* pr = part + static_cast<size_t>(m) * d;
+    for (int c = threadIdx.x; c < d / 4; c += 256) {
+      float4 v = src[c];
+      const float4 a = sum_planes(pr + 4 * c, plane, S);
+      v.x += a.x;
+      v.y += a.y;
+      v.z += a.z;
+      v.w += a.w;
+      sum_row[c] = v;
+      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
+    src = sum_row;
+  } else {
+    for (int c = threadIdx.x; c < d / 4; c += 256) {
+      const float4 v = src[c];
+      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
   }
+  // block_sum_256 synchronises the block: sum_row is complete after it (the
+  // loop below reads quads that other threads wrote)
   const float rstd = rsqrtf(block_sum_256(ss, red) / d + eps);
   for (int c = threadIdx.x; c < d / 8; c += 256) {
-    const float4 v0 = reinterpret_cast<const float4*>(xr)[2 * c];
-    const float4 v1 = reinterpret_cast<const float4*>(xr)[2 * c + 1];
+    const float4 v0 = src[2 * c];
+    const float4 v1 = src[2 * c + 1];
     float gg[8];
     unpack8(ld16(g + c * 8), gg);
     u32x4 o;
@@ -538,10 +560,11 @@ __global__ void __launch_bounds__(256) k_masked_norm(const uint8_t* __restrict__
 }
 
 hipError_t masked_norm(const uint8_t* masked, int M, const float* x, int d, const void* gain, float eps, void* xn,
-                       int* rows, int* count, hipStream_t s) {
+                       int* rows, int* count, hipStream_t s, const float* part, int S) {
   if (M <= 0) return hipSuccess;
+  if (d > 8192 || S < 0 || S > SPLIT_MAX || (S > 0 && !part)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_masked_norm, dim3(M), dim3(256), 0, s, masked, M, x, d, static_cast<const bf16_t*>(gain), eps,
-                     static_cast<bf16_t*>(xn), rows, count);
+                     static_cast<bf16_t*>(xn), rows, count, part, S);
   return hipGetLastError();
 }
 
