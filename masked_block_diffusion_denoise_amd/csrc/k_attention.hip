@@ -37,7 +37,11 @@
 namespace dlm {
 
 constexpr int KT = 32;          // keys per tile
-constexpr int MIN_CHUNK = 256;  // minimum keys per split (8 tiles)
+// Minimum keys per split (4 tiles).  Short prefixes at batch 1 are latency-
+// bound: shorter splits shorten each workgroup's chain of dependent tiles (the
+// 8B-class model over a ~1024-position prefix: 4.074 -> 4.023 ms per denoise
+// step with 128 instead of 256; 64 measured the same as 128).
+constexpr int MIN_CHUNK = 128;
 // Launch shape: up to 512 workgroups (two per CU, each with its 64 KB ring), so
 // that the other workgroup on a CU hides the latency of a stage's dependent
 // chain (one workgroup per CU with a deeper ring measured up to 25% slower at
