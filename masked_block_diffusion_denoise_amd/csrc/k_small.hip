@@ -28,6 +28,11 @@ namespace dlm {
 // the masked positions (float32 sum in position order) is below stop_entropy,
 // every remaining mask is committed.  prev_argmax takes this step's argmax.
 // Rows with no mask left are frozen (no state changes).
+// Lane i's value of v, i uniform (a scalar read, no LDS round trip).
+__device__ __forceinline__ float lane_value(float v, int i) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), i));
+}
+
 __device__ __forceinline__ bool commit_better(bool by_entropy, float ci, float ei, int i, float cj, float ej, int j) {
   if (by_entropy) return ei < ej || (ei == ej && i < j);
   return ci > cj || (ci == cj && i < j);
@@ -73,7 +78,7 @@ __global__ void __launch_bounds__(256) k_commit(const float* __restrict__ conf,
     const int stable = __any(diff) ? 0 : stable_in + 1;
     float total = 0.f;  // sequential, in position order
     for (int i = 0; i < L; ++i) {
-      const float ei = __shfl(e, i, WAVE);
+      const float ei = lane_value(e, i);
       if ((mball >> i) & 1ull) total = total + ei;
     }
     const float mean = total / static_cast<float>(cnt);
@@ -86,7 +91,7 @@ __global__ void __launch_bounds__(256) k_commit(const float* __restrict__ conf,
   // rank among the masked positions by the rule's order
   int rank = 0;
   for (int i = 0; i < L; ++i) {
-    const float ci = __shfl(c, i, WAVE), ei = __shfl(e, i, WAVE);
+    const float ci = lane_value(c, i), ei = lane_value(e, i);
     const bool mi = (mball >> i) & 1ull;
     rank += (mi && commit_better(by_ent, ci, ei, i, c, e, lane)) ? 1 : 0;
   }
@@ -104,7 +109,7 @@ __global__ void __launch_bounds__(256) k_commit(const float* __restrict__ conf,
       float total = 0.f, mine = 0.f;
       for (int r = 0; r < cnt; ++r) {
         const int src = __ffsll(static_cast<long long>(__ballot(mk && rank == r))) - 1;
-        total = total + __shfl(e, src, WAVE);
+        total = total + lane_value(e, src);
         if (rank == r) mine = total;
       }
       inA = mk && mine <= o.entropy_bound;
@@ -120,7 +125,7 @@ __global__ void __launch_bounds__(256) k_commit(const float* __restrict__ conf,
     } else {  // A plus the best-ranked others up to q
       int orank = 0;
       for (int i = 0; i < L; ++i) {
-        const float ci = __shfl(c, i, WAVE), ei = __shfl(e, i, WAVE);
+        const float ci = lane_value(c, i), ei = lane_value(e, i);
         const bool oi = ((mball & ~aball) >> i) & 1ull;
         orank += (oi && commit_better(by_ent, ci, ei, i, c, e, lane)) ? 1 : 0;
       }
@@ -131,7 +136,7 @@ __global__ void __launch_bounds__(256) k_commit(const float* __restrict__ conf,
       const unsigned long long cball = __ballot(chosen);
       int crank = 0;
       for (int i = 0; i < L; ++i) {
-        const float ci = __shfl(c, i, WAVE), ei = __shfl(e, i, WAVE);
+        const float ci = lane_value(c, i), ei = lane_value(e, i);
         crank += (((cball >> i) & 1ull) && commit_better(by_ent, ci, ei, i, c, e, lane)) ? 1 : 0;
       }
       chosen = chosen && crank < o.max_transfer;
