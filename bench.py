@@ -108,9 +108,10 @@ TIMERS = {"lm_head": 0, "attention": 1, "gate_up": 2, "down": 3, "qkv": 4}
 # head epilogue's template argument and the tile (k_gemm_tiled<EPI, BN, BM, ...>,
 # EPI_HEAD = 3).  At batch 32 one head is two launches, 256-row and up-to-320-row
 # tiles, of which only one does the work (the other reads the row count and
-# exits); a head's bytes are the sum of the two.  Batch 1: 256 x 64 tiles.
+# exits); a head's bytes are the sum of the two.  Batch 1: 256 x 32 (up to 32 rows) or
+# 256 x 64 tiles.
 HEAD_KERNELS = {"lm_head_b32": [re.compile(r"k_gemm_tiled<3, 256, 256,"), re.compile(r"k_gemm_tiled<3, 256, 320,")],
-                "lm_head_b1": [re.compile(r"k_gemm_tiled<3, 256, 64,")]}
+                "lm_head_b1": [re.compile(r"k_gemm_tiled<3, 256, (32|64),")]}
 COPY_KERNEL = re.compile(r"copyBuffer")
 
 
