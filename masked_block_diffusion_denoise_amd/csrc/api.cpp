@@ -130,12 +130,18 @@ size_t head_part_records(const dlm_config& c, int R, bool bound) {
   return r;
 }
 
-// Workspace of the largest K-split layer projection over R rows (or, for a
-// bound, over any row count up to R).
-size_t layer_gemm_ws(const dlm_config& c, int R) {
+// Workspace of the largest K-split layer projection over R rows, or with
+// `bound` over every row count r <= R.  The split count of a product falls as
+// its rows fill more tiles, so S(r) * r is not monotone in r (the down
+// projection at 483 rows takes 8 splits, at 544 rows 6): the bound takes the
+// largest value over the row counts where it can peak.  S(r) only changes
+// where the count of 128-row (or 256-row) tiles changes, or at 64 rows (short
+// products: S does not depend on r), so within each interval (128(k-1), 128k]
+// S is constant and S * r peaks at its right end.
+size_t layer_gemm_ws(const dlm_config& c, int R, bool bound) {
   const int d = c.d_model, qd = c.n_heads * c.head_dim;
   size_t b = 0;
-  for (int r : {R, std::min(R, 64)}) {
+  auto at = [&](int r) {
     b = std::max(b, gemm_workspace_bytes(r, qkv_dim(c), d));
     b = std::max(b, gemm_workspace_bytes(r, d, qd));
     b = std::max(b, gemm_workspace_bytes(r, 2 * c.d_ffn, d));
@@ -144,6 +150,11 @@ size_t layer_gemm_ws(const dlm_config& c, int R) {
       b = std::max(b, gemm_workspace_bytes(r, rank, qd));
       b = std::max(b, gemm_workspace_bytes(r, d, rank));
     }
+  };
+  at(R);
+  if (bound) {
+    at(std::min(R, 64));
+    for (int r = 128; r < R; r += 128) at(r);
   }
   return b;
 }
@@ -164,7 +175,7 @@ PassBufs carve(const dlm_config& c, uintptr_t base, int R, int B, int Lq, int ma
   p.rows = cv.take<int>(R);
   p.count = cv.take<int>(1);
   p.head_part = cv.take<float4>(head_part_records(c, R, bound));
-  p.kpart = cv.take<float>(layer_gemm_ws(c, R) / sizeof(float));
+  p.kpart = cv.take<float>(layer_gemm_ws(c, R, bound) / sizeof(float));
   p.lora_t = cv.take<bf16_t>(static_cast<size_t>(R) * DLM_MAX_LORA_RANK);
   p.bytes = align256(cv.off);
   return p;
@@ -501,12 +512,21 @@ dlm_status dlm_prefill(const dlm_model* m, const dlm_kv* kv, const int32_t* toke
     return fail(DLM_ERR_INVALID_ARG, "tokens/prefix_len NULL or misaligned");
   if ((last_argmax == nullptr) != (last_conf == nullptr))
     return fail(DLM_ERR_INVALID_ARG, "last_argmax and last_conf must both be given or both NULL");
-  // passes of C positions: C = T if it fits, else the largest multiple of 32 that does
+  // Passes of C positions: C = T if it fits, else the largest multiple of 32
+  // that does.  Every pass (the shorter last one included, and every prefix
+  // length a pass reads) is covered by the bound over B*C rows and T keys:
+  // each buffer of a pass is no larger than its bound.
   int C = T;
-  auto need = [&](int cc) { return carve(m->c, 0, B * cc, B, cc, T, false).bytes; };
+  auto need = [&](int cc) { return carve(m->c, 0, B * cc, 0, 0, T, true).bytes; };
   if (!ws || ws_bytes < need(C)) {
-    C = (T / 32) * 32;
-    while (C >= 32 && ws_bytes < need(C)) C -= 32;
+    // the bound grows with the rows: binary search over multiples of 32
+    int lo = 0, hi = T / 32;  // need(32 lo) fits (lo = 0: none yet), need(32 (hi + 1)) does not
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) / 2;
+      if (ws_bytes >= need(32 * mid)) lo = mid;
+      else hi = mid - 1;
+    }
+    C = 32 * lo;
     if (C < 32) return fail(DLM_ERR_WORKSPACE, "workspace %zu bytes cannot hold a 32-position pass (%zu)", ws_bytes,
                             need(std::min(T, 32)));
   }

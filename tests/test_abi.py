@@ -96,6 +96,34 @@ def test_workspace_bytes_grows_with_rows_and_keys(model):
     assert a % 256 == 0
 
 
+def test_workspace_bound_never_shrinks_with_rows():
+    """dlm_prefill sizes every pass (the shorter last one included) with the bound
+    over B*C rows.  A product's K-split count falls as its rows fill more tiles,
+    so the split workspace S(r) * r is not monotone in r (8B-class down
+    projection: 8 splits at 483 rows, 6 at 544); the bound must still never
+    shrink as rows grow, or a short last pass writes past the workspace."""
+    lib = L.load()
+    cfgs = [tiny_cfg(),
+            tiny_cfg(n_layers=32, d_model=4096, n_heads=32, n_kv_heads=8, head_dim=128, d_ffn=14336,
+                     vocab=131072, mask_id=100, rope_base=1e6)]
+    for cfg in cfgs:
+        st, h = create(cfg)
+        assert st == 0
+        try:
+            for kv in (64, 1027, 4128):
+                prev = 0
+                for r in range(1, 1100):
+                    b = lib.dlm_workspace_bytes(h, r, kv)
+                    assert b >= prev, (cfg.d_model, kv, r, b, prev)
+                    prev = b
+            if cfg.d_model == 4096:
+                # the 483-row down projection's eight fp32 partial planes fit the
+                # bound of a 544-row pass (whose own split count is only 6)
+                assert lib.dlm_workspace_bytes(h, 544, 1027) >= 8 * 483 * 4096 * 4
+        finally:
+            lib.dlm_model_destroy(h)
+
+
 def test_denoise_step_validation(model):
     lib = L.load()
     kv = L.KV(4096, 4096, 2, 128)

@@ -8,6 +8,7 @@ import numpy as np
 import pytest
 import torch
 
+import bf16_storage
 import oracle
 import synth
 from gpu_helpers import announce, host, i32, rel_rms, sync
@@ -17,7 +18,6 @@ from masked_block_diffusion_denoise_amd import runtime as R
 pytestmark = pytest.mark.gpu
 
 GAIN = 30.0          # wide top-1 margins for the token-sequence comparisons
-DENOISE_GAIN = 20.0  # the gain of the other denoise parity tests (confidences well inside (0, 1))
 
 
 @pytest.fixture(scope="module")
@@ -47,11 +47,17 @@ def sure_prefix(margins):
     return int(bad[0]) if len(bad) else len(margins)
 
 
+@pytest.mark.parametrize("gain", [20.0, 30.0])
 @pytest.mark.parametrize("enabled", [True, False])
-def test_denoise_with_adapter(tiny, enabled):
-    announce(f"lora denoise enabled={enabled}")
+def test_denoise_with_adapter(tiny, enabled, gain):
+    """The adapter's denoise pass against the oracle.  Confidences within 1e-2;
+    at a head gain of 30 bf16 storage alone moves them by more than that (the
+    oracle's arithmetic with the device's bf16 storage points: ~0.014 without
+    the adapter, ~0.010 with it), and the bar is twice that instead; at a gain
+    of 20 the 1e-2 bar itself holds."""
+    announce(f"lora denoise enabled={enabled} gain={gain}")
     _, lora, prompt, _ = tiny
-    w = synth.model_weights(TINY, seed=0, lm_head_gain=DENOISE_GAIN)
+    w = synth.model_weights(TINY, seed=0, lm_head_gain=gain)
     m = R.DlmModel.from_arrays(R.ModelConfig.of(TINY), w)
     m.set_lora(lora)
     sess = R.Session(m, 1, 128, 16)
@@ -75,8 +81,17 @@ def test_denoise_with_adapter(tiny, enabled):
         fin = np.isfinite(lo[j])
         assert rel_rms(got[j][fin], lo[j][fin]) < 2e-2, j
     conf_o, _ = oracle.confidence(lo)
-    mk = masked[0] != 0
-    assert np.abs(host(sess.conf)[0][mk] - conf_o[mk]).max() < 1e-2
+    lo16 = bf16_storage.denoise_logits(w, TINY, bf16_storage.prefill(w, TINY, prompt[0]), canvas[0],
+                                       lora=lora if enabled else None)
+    conf_16, _ = oracle.confidence(lo16)
+    mk = np.flatnonzero(masked[0])
+    err = np.abs(host(sess.conf)[0][mk] - conf_o[mk]).max()
+    bar = bf16_storage.conf_bar(conf_o, conf_16, mk)
+    print(f"[gpu-test] conf error {err:.4f}, bf16 storage alone {np.abs(conf_16 - conf_o)[mk].max():.4f}, "
+          f"bar {bar:.4f}", flush=True)
+    assert err <= bar
+    if gain == 20.0:
+        assert err < 1e-2
     m.set_lora(None)
 
 

@@ -122,6 +122,22 @@ def test_mask_token_is_never_predicted():
     assert np.isneginf(logits[:, TINY.mask_id]).all()
 
 
+def test_head_logits_apply_the_final_norm_hand_values():
+    # x = [3, 4]: mean square 12.5, so the normalised row is [3, 4] / 3.5355339 =
+    # [0.8485281, 1.1313708] (eps 1e-5 moves the 7th digit); head rows [1, 0],
+    # [0, 1], [1, 1] read it out, and the final-norm gains scale it per column.
+    shape = dataclasses.replace(TINY, d_model=2, vocab=4, mask_id=0)
+    head = np.array([[7.0, 7.0], [1.0, 0.0], [0.0, 1.0], [1.0, 1.0]])
+    lo = oracle.head_logits({"final_norm": np.array([1.0, 1.0]), "lm_head": head}, shape, np.array([[3.0, 4.0]]))
+    assert np.isneginf(lo[0, 0])
+    np.testing.assert_allclose(lo[0, 1:], [0.8485281, 1.1313708, 1.9798990], atol=2e-6)
+    lo = oracle.head_logits({"final_norm": np.array([2.0, 0.5]), "lm_head": head}, shape, np.array([[3.0, 4.0]]))
+    np.testing.assert_allclose(lo[0, 1:], [1.6970563, 0.5656854, 2.2627417], atol=2e-6)
+    # scaling the residual row leaves the logits unchanged (the norm removes it)
+    lo2 = oracle.head_logits({"final_norm": np.array([2.0, 0.5]), "lm_head": head}, shape, np.array([[30.0, 40.0]]))
+    np.testing.assert_allclose(lo2, lo, atol=1e-6)
+
+
 def test_greedy_ar_with_cache_equals_recompute():
     w = synth.model_weights(TINY, seed=6, lm_head_gain=20.0)
     prompt = synth.prompt(TINY, 1, 7, seed=6)[0]
