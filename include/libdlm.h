@@ -20,7 +20,8 @@
  * Conventions for every call:
  *   - [dev] pointers are device memory owned by the caller; [host] pointers are
  *     host memory owned by the caller.  The library keeps no pointer past the
- *     call except the weight pointers borrowed by a dlm_model.
+ *     call except the weight pointers borrowed by a dlm_model (and, per GPU,
+ *     the address of its own fixed scratch array, dlm_denoise_step_noalloc).
  *   - The library never allocates or frees device memory and never
  *     synchronises.  Work is enqueued on `stream` (a hipStream_t; NULL is the
  *     default stream) and may still be running when the call returns.
@@ -187,6 +188,28 @@ dlm_status dlm_denoise_step_ex(const dlm_model* m, const dlm_kv* kv, const int32
                                const int32_t* canvas, const uint8_t* masked, int32_t B, int32_t L, float* conf,
                                int32_t* argmax, float* entropy, float* logits, int32_t* flags, void* ws,
                                size_t ws_bytes, void* stream);
+
+/* dlm_denoise_step_ex without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, serving loops and
+ * harnesses that forbid allocation.  The pass's scratch is a fixed array of
+ * DLM_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, resident on each
+ * GPU the library has run this call on until the process ends; the call
+ * allocates nothing (no hipMalloc, no library allocation).  The array's device
+ * address is taken on the first call on a device, with that device current;
+ * call it with the device of `stream` current.  64 MiB holds a batch-1 pass of
+ * the 8B-class model (32 canvas positions) up to a 65536-position prefix;
+ * dlm_workspace_bytes bounds what a pass needs.  Every call on one GPU uses
+ * that GPU's one array, which keeps the last call's contents: calls that
+ * overlap on one GPU (other streams, other threads) race; calls on one stream
+ * are ordered.  Arguments, outputs and results as dlm_denoise_step_ex.
+ * Errors as dlm_denoise_step_ex; WORKSPACE (before any device call) if the
+ * pass needs more than DLM_NOALLOC_SCRATCH_BYTES; HIP if the scratch's device
+ * address cannot be obtained. */
+#define DLM_NOALLOC_SCRATCH_BYTES (64u << 20)
+dlm_status dlm_denoise_step_noalloc(const dlm_model* m, const dlm_kv* kv, const int32_t* prefix_len,
+                                    int32_t max_prefix, const int32_t* canvas, const uint8_t* masked, int32_t B,
+                                    int32_t L, float* conf, int32_t* argmax, float* entropy, float* logits,
+                                    int32_t* flags, void* stream);
 
 /* Commit / remask (MLX guide, sec. 5.2 native sampler and sec. 6; DiffusionGemma
  * docs, BlockRefinementScheduler).  Per row b with at least one masked position:

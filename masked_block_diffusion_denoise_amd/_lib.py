@@ -12,6 +12,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdlm.so")
 
 DLM_OK = 0
+NOALLOC_SCRATCH_BYTES = 64 << 20   # DLM_NOALLOC_SCRATCH_BYTES
 STATUS = {0: "DLM_OK", -1: "DLM_ERR_INVALID_ARG", -2: "DLM_ERR_SHAPE", -3: "DLM_ERR_CAPACITY",
           -4: "DLM_ERR_UNSUPPORTED", -5: "DLM_ERR_HIP", -6: "DLM_ERR_WORKSPACE"}
 
@@ -22,7 +23,7 @@ TIMER_LM_HEAD, TIMER_ATTENTION, TIMER_GATE_UP, TIMER_DOWN, TIMER_QKV = 0, 1, 2, 
 EXPORTS = [
     "dlm_model_create", "dlm_model_destroy", "dlm_model_set_lora", "dlm_model_enable_lora",
     "dlm_workspace_bytes", "dlm_prefill", "dlm_denoise_step", "dlm_denoise_step_ex",
-    "dlm_commit", "dlm_commit_ex", "dlm_append_block", "dlm_status_string", "dlm_last_error", "dlm_set_kernel_timer",
+    "dlm_commit", "dlm_commit_ex", "dlm_append_block", "dlm_denoise_step_noalloc", "dlm_status_string", "dlm_last_error", "dlm_set_kernel_timer",
     "dlm_op_gemm_workspace_bytes", "dlm_op_gemm", "dlm_op_rmsnorm", "dlm_op_rope_workspace_bytes",
     "dlm_op_rope_kv", "dlm_op_attention_workspace_bytes", "dlm_op_attention",
     "dlm_op_lm_head_workspace_bytes", "dlm_op_lm_head",
@@ -77,6 +78,7 @@ _SIGS = {
     "dlm_denoise_step": (i32, [vp, C.POINTER(KV), vp, i32, vp, vp, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
     "dlm_commit": (i32, [vp, vp, vp, vp, i32, i32, vp, vp, vp, i32, vp, vp, vp]),
     "dlm_denoise_step_ex": (i32, [vp, C.POINTER(KV), vp, i32, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]),
+    "dlm_denoise_step_noalloc": (i32, [vp, C.POINTER(KV), vp, i32, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp]),
     "dlm_commit_ex": (i32, [vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, i32, C.POINTER(CommitOpts), vp, vp, vp]),
     "dlm_append_block": (i32, [vp, C.POINTER(KV), vp, i32, vp, i32, i32, vp, vp, vp, vp, sz, vp]),
     "dlm_status_string": (C.c_char_p, [i32]),

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -607,6 +608,54 @@ dlm_status dlm_denoise_step_ex(const dlm_model* m, const dlm_kv* kv, const int32
                       splits),
           "masked rows + final norm");
   return run_head(m, R, p.rows, p.count, p.rows, conf, argmax, logits, flags, p, s, true, false, entropy);
+}
+
+// ----------------------------------------------- allocation-free step ----
+// The scratch of dlm_denoise_step_noalloc: one fixed array per GPU, in the code
+// object's device memory.  In host code `scratch` names a host-side stand-in,
+// not a device address: the device address comes from hipGetSymbolAddress,
+// taken once per device with that device current, and only that address is
+// handed to kernels.
+static __device__ __align__(256) unsigned char scratch[DLM_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+dlm_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  DLM_TRY(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(DLM_ERR_HIP, "device %d outside [0, %d)", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    DLM_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (!p || (reinterpret_cast<uintptr_t>(p) & 255u)) return fail(DLM_ERR_HIP, "scratch address %p unusable", p);
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return DLM_OK;
+}
+}  // namespace
+
+dlm_status dlm_denoise_step_noalloc(const dlm_model* m, const dlm_kv* kv, const int32_t* prefix_len,
+                                    int32_t max_prefix, const int32_t* canvas, const uint8_t* masked, int32_t B,
+                                    int32_t L, float* conf, int32_t* argmax, float* entropy, float* logits,
+                                    int32_t* flags, void* stream) {
+  g_err[0] = 0;
+  dlm_status st = check_block_call(m, kv, prefix_len, max_prefix, canvas, B, L);
+  if (st != DLM_OK) return st;
+  // the pass's exact workspace (the same carve dlm_denoise_step_ex makes),
+  // checked against the fixed scratch before any device call
+  const size_t need = carve(m->c, 0, B * L, B, L, max_prefix + L, false).bytes;
+  if (need > DLM_NOALLOC_SCRATCH_BYTES)
+    return fail(DLM_ERR_WORKSPACE, "this pass needs %zu bytes of scratch, the fixed scratch holds %zu", need,
+                static_cast<size_t>(DLM_NOALLOC_SCRATCH_BYTES));
+  void* ws = nullptr;
+  if ((st = scratch_of_current_device(&ws)) != DLM_OK) return st;
+  return dlm_denoise_step_ex(m, kv, prefix_len, max_prefix, canvas, masked, B, L, conf, argmax, entropy, logits,
+                             flags, ws, DLM_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 dlm_status dlm_commit(const float* conf, const int32_t* argmax, int32_t* canvas, uint8_t* masked, int32_t B,

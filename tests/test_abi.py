@@ -150,6 +150,28 @@ def test_denoise_step_validation(model):
     assert b"workspace" in lib.dlm_last_error()
 
 
+def test_noalloc_step_validation_and_scratch_limit():
+    """The allocation-free step validates like dlm_denoise_step_ex and refuses a
+    pass larger than its fixed scratch before any device call."""
+    lib = L.load()
+    st, h = create(tiny_cfg(n_layers=1, d_model=4096, n_heads=32, n_kv_heads=8, head_dim=128, d_ffn=14336,
+                            vocab=131072, mask_id=100, rope_base=1e6))
+    assert st == 0
+    try:
+        run = lambda B, Lb, P, cap=8192, canvas=FAKE: lib.dlm_denoise_step_noalloc(
+            h, C.byref(L.KV(4096, 4096, 32, cap)), FAKE, P, canvas, FAKE, B, Lb, FAKE, FAKE, None, None, None, None)
+        assert run(0, 32, 4096) == -2
+        assert run(1, 65, 4096) == -2
+        assert run(1, 32, 8192) == -3
+        assert run(1, 32, 4096, canvas=None) == -1
+        assert L.NOALLOC_SCRATCH_BYTES == 64 << 20
+        assert lib.dlm_workspace_bytes(h, 32 * 32, 4096 + 32) > L.NOALLOC_SCRATCH_BYTES
+        assert run(32, 32, 4096) == -6                 # batch 32 needs more than 64 MiB
+        assert b"scratch" in lib.dlm_last_error()
+    finally:
+        lib.dlm_model_destroy(h)
+
+
 def test_commit_validation():
     lib = L.load()
     f = FAKE
