@@ -9,7 +9,12 @@ N(0, 0.02) bf16 from a fixed seed.  One step = restore the canvas, one
 dlm_denoise_step, one dlm_commit; inputs are resident in HBM before timing.
 
 Prints one JSON line.  Per-kernel times come from HIP events that the library
-records around the kernel inside the real step (dlm_set_kernel_timer).
+records around the kernel inside the real step (dlm_set_kernel_timer).  The
+single-layer steps rotate over three copies of the layer weights and of the KV
+prefix (the last-level cache holds 256 MB; one copy would let a step reuse the
+previous step's weights, which a 32-layer model never can); the median and
+p10/p90 of per-step event times are reported beside the wall-clock mean, with
+the GPU clock sampled during the timed steps and the ROCm version.
 
 The same line carries, under "e2e", the full 32-layer 8B-class model (random
 N(0, 0.02) bf16 weights drawn on the device): block-diffusion decoding at batch
@@ -102,7 +107,8 @@ def traffic_for(kernel: str, batch: int):
         return None
 
 
-TIMERS = {"lm_head": 0, "attention": 1, "gate_up": 2, "down": 3, "qkv": 4}
+TIMERS = {"lm_head": 0, "attention": 1, "gate_up": 2, "down": 3, "qkv": 4, "o_proj": 5, "final_norm": 6}
+ROTATE = 3   # weight/KV copies the single-layer steps rotate over
 
 # LM-head launches in a counter run, told apart from the other GEMMs by the
 # head epilogue's template argument and the tile (k_gemm_tiled<EPI, BN, BM, ...>,
@@ -166,7 +172,83 @@ def traffic_from(fetch_dir: str, write_dir: str, copy_mib: int, command: str) ->
     return out
 
 
-def run_batch(model, shape, B, steps, warmup, P=4096, Lb=32, seed=3):
+def _pct(xs, q):
+    import numpy as np
+    return round(float(np.percentile(np.asarray(xs), q)), 4)
+
+
+class ClockSampler:
+    """Samples the GPU's current shader clock (sysfs pp_dpm_sclk, the '*' level)
+    in a thread while the timed steps run; no-op where sysfs is not readable."""
+
+    def __init__(self, period_s=0.02):
+        import glob
+        import threading
+        self.paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.samples, self.period = [], period_s
+        self._stop = threading.Event()
+        self._t = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        for pth in self.paths:
+            try:
+                for line in open(pth):
+                    if line.rstrip().endswith("*"):
+                        m = re.search(r"(\d+)\s*[Mm][Hh]z", line)
+                        if m:
+                            return int(m.group(1))
+            except OSError:
+                continue
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            v = self._read()
+            if v is not None:
+                self.samples.append(v)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.paths:
+            self._t.start()
+        return self
+
+    def __exit__(self, *a):
+        self._stop.set()
+        if self.paths:
+            self._t.join(timeout=2)
+
+    def summary(self):
+        if not self.samples:
+            return None
+        xs = sorted(self.samples)
+        return {"samples": len(xs), "min_mhz": xs[0], "median_mhz": xs[len(xs) // 2], "max_mhz": xs[-1]}
+
+
+def gpu_info() -> dict:
+    import torch
+    out = {"device": torch.cuda.get_device_name(0), "hip_runtime": torch.version.hip}
+    try:
+        out["rocm"] = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        out["rocm"] = None
+    return out
+
+
+def layer_copies(model, n):
+    """``model`` and n - 1 copies of its layer weights on the device (embedding,
+    final norm and the 1 GB head shared)."""
+    from masked_block_diffusion_denoise_amd import runtime as R
+    out = [model]
+    for _ in range(n - 1):
+        t = dict(model.t)
+        for k in ("attn_norm", "wqkv", "wo", "ffn_norm", "wgu", "wdown"):
+            t[k] = [x.clone() for x in model.t[k]]
+        out.append(R.DlmModel(model.cfg, t, model.device))
+    return out
+
+
+def run_batch(models, shape, B, steps, warmup, P=4096, Lb=32, seed=3):
     import numpy as np
     import torch
 
@@ -174,12 +256,17 @@ def run_batch(model, shape, B, steps, warmup, P=4096, Lb=32, seed=3):
     from masked_block_diffusion_denoise_amd import _lib as L
     from masked_block_diffusion_denoise_amd import runtime as R
 
-    sess = R.Session(model, B, P + Lb + 64, Lb)
     k, v = synth.kv_prefix(shape, B, P, seed=seed)
-    sess.kv.write(0, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda())
+    kt, vt = torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda()
     del k, v
-    sess.prefix.fill_(P)
-    sess.max_prefix = P
+    sessions = []
+    for m in models:        # one KV prefix per weight copy: a step reads neither the previous one's
+        sess = R.Session(m, B, P + Lb + 64, Lb)
+        sess.kv.write(0, kt, vt)
+        sess.prefix.fill_(P)
+        sess.max_prefix = P
+        sessions.append(sess)
+    del kt, vt
     canvas, masked = synth.ragged_canvas(shape, B, Lb, seed=seed)
     tc = torch.from_numpy(canvas).cuda()
     tm = torch.from_numpy(masked).cuda()
@@ -189,70 +276,151 @@ def run_batch(model, shape, B, steps, warmup, P=4096, Lb=32, seed=3):
     ev = HipEvents()
     lib = L.load()
 
-    def step():
+    def step(sess):
         sess.canvas.copy_(tc)
         sess.masked.copy_(tm)
         sess.steps.zero_()
         sess.denoise_step()
         sess.commit(tau, quota, max_steps)
 
-    for _ in range(warmup):
-        step()
+    n = len(sessions)
+    for i in range(warmup):
+        step(sessions[i % n])
     torch.cuda.synchronize()
-    pairs = {n: [(ev.new(), ev.new()) for _ in range(steps)] for n in TIMERS}
+    pairs = {nm: [(ev.new(), ev.new()) for _ in range(steps)] for nm in TIMERS}
+    step_ev = [(ev.new(), ev.new()) for _ in range(steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        for n, kid in TIMERS.items():
-            lib.dlm_set_kernel_timer(kid, pairs[n][i][0], pairs[n][i][1])
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    with ClockSampler() as clk:
+        t0 = time.perf_counter()
+        for i in range(steps):
+            for nm, kid in TIMERS.items():
+                lib.dlm_set_kernel_timer(kid, pairs[nm][i][0], pairs[nm][i][1])
+            ev.record(step_ev[i][0])
+            step(sessions[i % n])
+            ev.record(step_ev[i][1])
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
     for kid in TIMERS.values():
         lib.dlm_set_kernel_timer(kid, None, None)
     ms_step = (t1 - t0) * 1e3 / steps
-    kms = {n: sum(ev.ms(a, b) for a, b in pairs[n]) / steps for n in TIMERS}
+    per_step = [ev.ms(a, b) for a, b in step_ev]
+    kms = {nm: [ev.ms(a, b) for a, b in pairs[nm]] for nm in TIMERS}
+    # the same steps on one weight/KV copy: what the last-level cache gives back
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for _ in range(steps):
+        step(sessions[0])
+    torch.cuda.synchronize()
+    one_copy_ms = (time.perf_counter() - t2) * 1e3 / steps
     ev.close()
-    committed = int(sess.n_committed.sum().item())
-    flags = sess.flags.cpu().tolist()
+    last = sessions[(steps - 1) % n]
+    committed = int(last.n_committed.sum().item())
+    flags = [int(x) for s_ in sessions for x in s_.flags.cpu().tolist()]
     mrows = int(masked.sum())
     kernels = {}
-    for n, t in kms.items():
-        by, fl = RL.kernel_work(n, B, Lb, P, mrows, shape.d_model, shape.n_heads, shape.n_kv_heads,
-                                shape.head_dim, shape.d_ffn, shape.vocab)
-        kernels[n] = {"ms": round(t, 4), "bytes": by, "flops": fl,
-                      "roofline": RL.roofline(by, fl, t, traffic_for(n, B))}
+    for nm, ts in kms.items():
+        t = sum(ts) / len(ts)
+        rec = {"ms": round(t, 4), "ms_median": _pct(ts, 50)}
+        if nm != "final_norm":
+            by, fl = RL.kernel_work(nm, B, Lb, P, mrows, shape.d_model, shape.n_heads, shape.n_kv_heads,
+                                    shape.head_dim, shape.d_ffn, shape.vocab)
+            rec.update(bytes=by, flops=fl, roofline=RL.roofline(by, fl, t, traffic_for(nm, B)))
+        kernels[nm] = rec
+    # The last layer's down projection, when split over K, leaves its partial
+    # products to the final norm of the masked rows (final_norm), so "down"
+    # alone times only the partials: down + final_norm bounds it with its reduction.
+    dn = kernels["down"]
+    t = dn["ms"] + kernels["final_norm"]["ms"]
+    kernels["down_with_final_norm"] = {"ms": round(t, 4), "bytes": dn["bytes"], "flops": dn["flops"],
+                                       "roofline": RL.roofline(dn["bytes"], dn["flops"], t, None)}
     return {"batch": B, "ms_per_step": ms_step, "steps_per_s": 1e3 / ms_step,
+            "step_ms": {"wall_mean": round(ms_step, 4), "median": _pct(per_step, 50), "p10": _pct(per_step, 10),
+                        "p90": _pct(per_step, 90), "one_copy_wall_mean": round(one_copy_ms, 4)},
+            "gpu_clock": clk.summary(),
             "committed_per_step": committed, "committed_tokens_per_s": committed * 1e3 / ms_step,
             "masked_rows": mrows, "kernels": kernels, "flags": flags,
             "inputs": (canvas, masked)}
 
 
-def cpu_baseline(w, shape, B, canvas, masked, P=4096, seed=3, rows=16):
-    """The oracle (float64 NumPy) on a bounded sample: `rows` batch rows of the step."""
+def blas_setup():
+    """The BLAS thread count for the oracle: the host's CPU share (the affinity
+    set, capped by OMP_NUM_THREADS where the machine sets it), set explicitly."""
+    n = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    info = {"threads": n, "affinity_cpus": len(os.sched_getaffinity(0)), "blas": None, "cpu_model": None}
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            info["blas"] = f"{libs[0].get('internal_api')} {libs[0].get('version')}"
+    except Exception:
+        pass
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                info["cpu_model"] = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return info
+
+
+def cpu_baseline(w, shape, inputs, P=4096, sample_rows=8):
+    """The oracle (float64 NumPy) on bounded samples of the configured workloads:
+    the one-layer step at batch 32 (``sample_rows`` rows, scaled to the batch; the
+    headline leg), the same step at batch 1, and config 1 (the tiny model) end to end."""
     import numpy as np
 
     import oracle
     import synth
+    import contextlib
+    info = blas_setup()
     try:
-        from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(limits=info["threads"], user_api="blas")
     except Exception:
-        threads = len(os.sched_getaffinity(0))
-    k, v = synth.kv_prefix(shape, min(rows, B), P, seed=seed) if B >= rows else synth.kv_prefix(shape, B, P, seed)
-    n = min(rows, B)
-    t0 = time.perf_counter()
-    for b in range(n):
-        cache = oracle.KVCache(shape)
-        cache.k[0] = k[b].astype(np.float64)
-        cache.v[0] = v[b].astype(np.float64)
-        lo = oracle.denoise_logits(w, shape, cache, canvas[b])
-        conf, arg = oracle.confidence(lo)
-        oracle.commit(conf, arg, canvas[b], masked[b].astype(bool), 0.9, 1, 0, 32)
-    t = (time.perf_counter() - t0) / n
-    return {"value": round(1.0 / (t * B), 6), "unit": "denoise steps/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} of the {B} batch rows of one step (layer + head over all 32 canvas rows + commit, "
-                      f"float64 NumPy), {t:.2f} s per row, scaled to the whole batch"}
+        limit = contextlib.nullcontext()
+
+    def layer_rows(B, n):
+        canvas, masked = inputs[B]
+        k, v = synth.kv_prefix(shape, n, P, seed=3)
+        t0 = time.perf_counter()
+        for b in range(n):
+            cache = oracle.KVCache(shape)
+            cache.k[0] = k[b].astype(np.float64)
+            cache.v[0] = v[b].astype(np.float64)
+            lo = oracle.denoise_logits(w, shape, cache, canvas[b])
+            conf, arg = oracle.confidence(lo)
+            oracle.commit(conf, arg, canvas[b], masked[b].astype(bool), 0.9, 1, 0, 32)
+        return (time.perf_counter() - t0) / n
+
+    legs = {}
+    rows = min(sample_rows, 32)
+    with limit:
+        t32 = layer_rows(32, rows) if 32 in inputs else None
+        t1 = layer_rows(1, 1) if 1 in inputs else None
+        tiny = synth.TINY
+        wt = synth.model_weights(tiny, seed=0)
+        pr = synth.prompt(tiny, 1, 32, seed=0)[0]
+        t0 = time.perf_counter()
+        out, st, _ = oracle.generate_block_diffusion(wt, tiny, pr, 32, 16, 16, 0.9, 1)
+        tt = time.perf_counter() - t0
+    if t1 is not None:
+        legs["layer_step_b1"] = {"value": round(1.0 / t1, 6), "unit": "denoise steps/s",
+                                 "sample": "the whole batch-1 step (one row: layer + head + commit)"}
+    legs["tiny_e2e_b1"] = {"value": round(len(out) / tt, 3), "unit": "committed tokens/s",
+                           "denoise_steps_per_s": round(st.denoise_nfe / tt, 3),
+                           "sample": "the tiny model (2 layers, d 128, vocab 1024), 32-token prompt, 32 tokens in "
+                                     "2 blocks of 16, prefill and appends included"}
+    head = {"value": round(1.0 / (t32 * 32), 6), "unit": "denoise steps/s", "cores": info["threads"],
+            "kind": "oracle",
+            "sample": f"{rows} of the 32 batch rows of one batch-32 step (layer + head over all 32 canvas rows + "
+                      f"commit, float64 NumPy), {t32:.2f} s per row, scaled to the whole batch"} if t32 else {}
+    head.update({"cpu_model": info["cpu_model"], "blas": info["blas"], "affinity_cpus": info["affinity_cpus"],
+                 "legs": legs})
+    return head
 
 
 # ------------------------------------------------------------------ full model
@@ -462,6 +630,54 @@ def run_e2e(gen=256) -> dict:
     return res
 
 
+def assemble(res: dict, batches: list, steps: int, warmup: int, gpu: dict) -> dict:
+    """The bench line (one JSON object) from the per-batch results of run_batch."""
+    head = res[batches[0]]
+    B0 = batches[0]
+    timed = ("lm_head", "attention", "gate_up", "down", "qkv", "o_proj")
+    dom = max(timed, key=lambda n: head["kernels"][n]["ms"])
+    kern = lambda r: {n: {"ms": k["ms"], "ms_median": k.get("ms_median"), **k.get("roofline", {})}
+                      for n, k in r["kernels"].items()}
+    out = {
+        "metric": METRIC,
+        "value": round(head["steps_per_s"], 3),
+        "unit": "denoise steps/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(head["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded random-init N(0,0.02) bf16 weights, N(0,1) 4096-position KV prefix, "
+                "ragged ~50%-masked 32-position canvas",
+        "config": {"workload": f"one 8B-class decoder layer (d 4096, 32/8 heads x 128, SwiGLU 14336) + final "
+                               f"norm + fused 131072-vocab LM head to confidence + threshold-0.9 commit; "
+                               f"prefix 4096, canvas 32; batch {B0}; value = steps/s of this one-layer step "
+                               f"(full 32-layer model figures: e2e)",
+                   "global_batch": B0, "seq_len": 4096 + 32, "parallelism": "single GPU"},
+        "step_ms": head["step_ms"],
+        "timing": {"protocol": f"{warmup} untimed steps, then {steps} timed between two device syncs "
+                               f"(value, ms_per_step); per-step HIP events give median/p10/p90; the steps rotate "
+                               f"over {ROTATE} copies of the layer weights and KV prefix (one_copy_wall_mean: "
+                               f"the same steps on one copy)",
+                   "gpu_clock_during_steps": head["gpu_clock"], **gpu},
+        "single_layer_step_committed_tokens_per_s": round(head["committed_tokens_per_s"], 2),
+        "committed_per_step": head["committed_per_step"],
+        "dominant_kernel": dom,
+        "roofline": head["kernels"][dom]["roofline"],
+        "kernels": kern(head),
+    }
+    for B in batches[1:]:
+        r = res[B]
+        out[f"b{B}"] = {"steps_per_s": round(r["steps_per_s"], 3), "ms_per_step": round(r["ms_per_step"], 4),
+                        "step_ms": r["step_ms"], "gpu_clock_during_steps": r["gpu_clock"],
+                        "single_layer_step_committed_tokens_per_s": round(r["committed_tokens_per_s"], 2),
+                        "kernels": kern(r)}
+    return out
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -501,51 +717,25 @@ def main(argv=None) -> int:
     print(f"[bench] generating weights", file=sys.stderr, flush=True)
     w = synth.model_weights(shape, seed=0)
     model = R.DlmModel.from_arrays(R.ModelConfig.of(shape), w)
+    models = layer_copies(model, ROTATE)
     batches = [int(x) for x in a.batches.split(",")]
     res = {}
     for B in batches:
         print(f"[bench] batch {B}", file=sys.stderr, flush=True)
-        res[B] = run_batch(model, shape, B, a.steps, a.warmup)
-    head = res[batches[0]]
-    B0 = batches[0]
-    dom = max(head["kernels"], key=lambda n: head["kernels"][n]["ms"])
-    out = {
-        "metric": METRIC,
-        "value": round(head["steps_per_s"], 3),
-        "unit": "denoise steps/s",
-        "n_gpus": 1,
-        "steps": a.steps,
-        "warmup": a.warmup,
-        "ms_per_step": round(head["ms_per_step"], 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic: seeded random-init N(0,0.02) bf16 weights, N(0,1) 4096-position KV prefix, "
-                "ragged ~50%-masked 32-position canvas",
-        "config": {"workload": f"one 8B-class decoder layer (d 4096, 32/8 heads x 128, SwiGLU 14336) + final "
-                               f"norm + fused 131072-vocab LM head to confidence + threshold-0.9 commit; "
-                               f"prefix 4096, canvas 32; batch {B0}",
-                   "global_batch": B0, "seq_len": 4096 + 32, "parallelism": "single GPU"},
-        "committed_tokens_per_s": round(head["committed_tokens_per_s"], 2),
-        "committed_per_step": head["committed_per_step"],
-        "dominant_kernel": dom,
-        "roofline": head["kernels"][dom]["roofline"],
-        "kernels": {n: {"ms": k["ms"], **k["roofline"]} for n, k in head["kernels"].items()},
-    }
-    for B in batches[1:]:
-        r = res[B]
-        out[f"b{B}"] = {"steps_per_s": round(r["steps_per_s"], 3), "ms_per_step": round(r["ms_per_step"], 4),
-                        "committed_tokens_per_s": round(r["committed_tokens_per_s"], 2),
-                        "kernels": {n: {"ms": k["ms"], **k["roofline"]} for n, k in r["kernels"].items()}}
-    del model, res
+        res[B] = run_batch(models, shape, B, a.steps, a.warmup)
+    out = assemble(res, batches, a.steps, a.warmup, gpu_info())
+    inputs = {B: res[B]["inputs"] for B in batches}
+    del model, models, res
     torch.cuda.empty_cache()
     if not a.no_e2e:
         out["e2e"] = run_e2e()
+        out["model_committed_tokens_per_s"] = {
+            "b1": out["e2e"]["block_diffusion_b1"]["committed_tokens_per_s"],
+            "b32": out["e2e"]["block_diffusion_b32"]["committed_tokens_per_s"],
+            "note": "full 32-layer 8B-class model, decode after prefill (e2e.block_diffusion_*)"}
     if not a.no_cpu:
         print(f"[bench] cpu oracle baseline", file=sys.stderr, flush=True)
-        canvas, masked = head["inputs"]
-        out["cpu_baseline"] = cpu_baseline(w, shape, B0, canvas, masked)
+        out["cpu_baseline"] = cpu_baseline(w, shape, inputs)
     print(json.dumps(out), flush=True)
     return 0
 

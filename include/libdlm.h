@@ -291,11 +291,19 @@ dlm_status dlm_append_block(const dlm_model* m, const dlm_kv* kv, int32_t* prefi
  *   DLM_TIMER_LM_HEAD      the fused LM-head GEMM of dlm_denoise_step
  *   DLM_TIMER_ATTENTION    block attention (with its split merge) of the first layer
  *   DLM_TIMER_GATE_UP      the SwiGLU gate/up GEMM of the first layer
- *   DLM_TIMER_DOWN         the down-projection GEMM of the first layer
- *   DLM_TIMER_QKV          the fused QKV GEMM of the first layer
+ *   DLM_TIMER_DOWN         the down-projection GEMM of the first layer (with its residual
+ *                          add and the next RMSNorm; for the last layer, when split over
+ *                          K, only the partial products: DLM_TIMER_FINAL_NORM sums them)
+ *   DLM_TIMER_QKV          the fused QKV GEMM of the first layer (with its K-split
+ *                          reduction, fused with RoPE and the cache write, when split)
+ *   DLM_TIMER_O            the attention output projection of the first layer with its
+ *                          residual add and the FFN RMSNorm
+ *   DLM_TIMER_FINAL_NORM   masked-row compaction + final RMSNorm of dlm_denoise_step,
+ *                          which also sums the last layer's down-projection K-split
+ *                          partials when that product is split
  * Errors: INVALID_ARG for an unknown kernel id. */
 enum { DLM_TIMER_LM_HEAD = 0, DLM_TIMER_ATTENTION = 1, DLM_TIMER_GATE_UP = 2, DLM_TIMER_DOWN = 3,
-       DLM_TIMER_QKV = 4, DLM_TIMER_COUNT = 5 };
+       DLM_TIMER_QKV = 4, DLM_TIMER_O = 5, DLM_TIMER_FINAL_NORM = 6, DLM_TIMER_COUNT = 7 };
 dlm_status dlm_set_kernel_timer(int32_t kernel, void* start_event, void* stop_event);
 
 const char* dlm_status_string(dlm_status s);

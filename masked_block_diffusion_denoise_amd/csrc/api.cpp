@@ -293,7 +293,10 @@ dlm_status run_layers(const dlm_model* m, const dlm_kv* kv, const int32_t* token
     g.K = qd;
     g.lda = qd;
     g.ldc = d;
-    if ((st = resid_gemm(g, m->lora_on ? nullptr : m->ffn_norm[l], "gemm o")) != DLM_OK) return st;
+    {
+      TimerScope t(DLM_TIMER_O, s, l == 0);
+      if ((st = resid_gemm(g, m->lora_on ? nullptr : m->ffn_norm[l], "gemm o")) != DLM_OK) return st;
+    }
     if (m->lora_on) {  // x += scale * (o A^T) B^T, then the FFN norm
       GemmArgs la{};
       la.kpart = p.kpart;
@@ -604,9 +607,12 @@ dlm_status dlm_denoise_step_ex(const dlm_model* m, const dlm_kv* kv, const int32
   int splits = 0;
   if ((st = run_layers(m, kv, canvas, L, B, L, prefix_len, 0, 0, max_kv, flags, p, s, &splits)) != DLM_OK)
     return st;
-  DLM_TRY(masked_norm(masked, R, p.x, m->c.d_model, m->final_norm, m->c.rms_eps, p.xn, p.rows, p.count, s, p.kpart,
-                      splits),
-          "masked rows + final norm");
+  {
+    TimerScope t(DLM_TIMER_FINAL_NORM, s);
+    DLM_TRY(masked_norm(masked, R, p.x, m->c.d_model, m->final_norm, m->c.rms_eps, p.xn, p.rows, p.count, s,
+                        p.kpart, splits),
+            "masked rows + final norm");
+  }
   return run_head(m, R, p.rows, p.count, p.rows, conf, argmax, logits, flags, p, s, true, false, entropy);
 }
 

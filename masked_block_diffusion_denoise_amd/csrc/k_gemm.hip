@@ -215,11 +215,14 @@ __device__ __forceinline__ void lds_frags(uint32_t a, uint32_t b, u32x4 (&fa)[TN
 // With DYN the live rows (the device row count) are split evenly, in 32-row
 // units, over the fewest tiles of at most BM rows, so that a count just past a
 // multiple of the tile height does not cost one more pass over the weights;
-// tiles past that number exit.  With g.pick_rows set, two launches with
-// different tile heights cover one product and only the one that needs fewer
-// row tiles for the device row count runs (the shorter one on a tie).
+// tiles past that number exit.
+template <int BN, int BM, int NBUF, int BK>
+struct TileLds {
+  static constexpr int BYTES = NBUF * (BN + BM) * BK * 2;
+};
+
 template <int EPI, int BN, int BM, int WN, int WM, int NBUF, int BK, bool DYN>
-__global__ void __launch_bounds__(WN * WM * 64) k_gemm_tiled(GemmArgs g) {
+__device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* lds) {
   constexpr int T = WN * WM * 64;
   constexpr int TN = BN / WN / 32, TM = BM / WM / 32;
   constexpr int ROW = BK * 2, CH = BK / 8;         // bytes and 16-byte chunks per stage row
@@ -228,7 +231,6 @@ __global__ void __launch_bounds__(WN * WM * 64) k_gemm_tiled(GemmArgs g) {
   static_assert(STAGE % (1024 * (T / 64)) == 0, "stage must split into 1 KB blocks per wavefront");
   static_assert(BN % (1024 / ROW) == 0, "a 1 KB block must not straddle the weight/activation regions");
   static_assert(NBUF >= 2 && NBUF <= 6, "wait ladder covers up to four later stages");
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[NBUF * STAGE];
 
   // tile = (weight tile, K range, activation tile), activation tiles fastest.
   // The grid is sized for M rows; the tiles are laid out for the live rows, so
@@ -238,9 +240,6 @@ __global__ void __launch_bounds__(WN * WM * 64) k_gemm_tiled(GemmArgs g) {
   const int S = EPI == EPI_SPLITK ? g.ksplit : 1;
   const int live_rows = g.m_dev ? min(g.M, *g.m_dev) : g.M;
   const int nt = (live_rows + BM - 1) / BM;  // row tiles
-  if (g.pick_rows && (BM > g.pick_rows ? nt >= (live_rows + g.pick_rows - 1) / g.pick_rows
-                                       : nt > (live_rows + g.pick_rows - 1) / g.pick_rows))
-    return;
   const int total = g.N / BN * S * nt, per = (total + 7) / 8;
   if (static_cast<int>(blockIdx.x / 8) >= per) return;
   const int tid_ = (blockIdx.x % 8) * per + blockIdx.x / 8;
@@ -491,6 +490,31 @@ __global__ void __launch_bounds__(WN * WM * 64) k_gemm_tiled(GemmArgs g) {
   }
 }
 
+template <int EPI, int BN, int BM, int WN, int WM, int NBUF, int BK, bool DYN>
+__global__ void __launch_bounds__(WN * WM * 64) k_gemm_tiled(GemmArgs g) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[TileLds<BN, BM, NBUF, BK>::BYTES];
+  gemm_tile<EPI, BN, BM, WN, WM, NBUF, BK, DYN>(g, lds);
+}
+
+// The LM head over many scored rows, whose count only the device knows: every
+// row tile is one more pass of the 1 GB of weights through LDS, so the launch
+// takes 256-row tiles or the fewest tiles of up to 320 rows with the rows split
+// evenly, whichever needs fewer (256-row tiles on a tie; e.g. 530 rows: two
+// tiles of 288 rows instead of three of 256).  Both tile bodies live in this
+// one kernel behind a branch on the count (the grid is sized for 256-row
+// tiles, the larger count), which replaces a second launch that only read the
+// count and exited (~4 us per step).
+constexpr int HEAD_BM_MAX = 320;
+__global__ void __launch_bounds__(512) k_gemm_head_rows(GemmArgs g) {
+  constexpr int L256 = TileLds<256, 256, 2, 64>::BYTES, L320 = TileLds<256, HEAD_BM_MAX, 2, 64>::BYTES;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[L256 > L320 ? L256 : L320];
+  const int live = g.m_dev ? min(g.M, *g.m_dev) : g.M;
+  if ((live + 255) / 256 <= (live + HEAD_BM_MAX - 1) / HEAD_BM_MAX)
+    gemm_tile<EPI_HEAD, 256, 256, 4, 2, 2, 64, false>(g, lds);
+  else
+    gemm_tile<EPI_HEAD, 256, HEAD_BM_MAX, 4, 2, 2, 64, true>(g, lds);
+}
+
 // Sum of the K-split partials in split order (deterministic), then the
 // epilogue; one thread per 4 output columns of one row.
 template <int EPI>
@@ -603,9 +627,8 @@ static hipError_t launch_epi(const GemmArgs& g, hipStream_t s) {
     // and short tiles whose activation rows every wavefront shares from LDS, two
     // workgroups per CU, keep the most bytes in flight.  Above that, every row
     // tile is one more pass of the weights through LDS, and the scored-row count
-    // is known only on the device: 256-row tiles and tiles of up to 320 rows
-    // split evenly are both launched, and only the one needing fewer row tiles
-    // runs (e.g. 530 rows: two tiles of 288 rows instead of three).
+    // is known only on the device: one launch picks 256-row tiles or tiles of
+    // up to 320 rows split evenly, whichever needs fewer (k_gemm_head_rows).
     if (g.M <= 32) {
       // one 32-row fragment per wavefront: a tenth fewer bytes per stage through
       // LDS than the 64-row tile (batch 1: 0.158 -> 0.156 ms)
@@ -616,14 +639,12 @@ static hipError_t launch_epi(const GemmArgs& g, hipStream_t s) {
       launch_tiled<EPI, 256, 64, 4, 1, 2, 64>(g, s);
     } else if (g.M <= 128) {
       launch_tiled<EPI, 256, 128, 4, 2, 3>(g, s);
+    } else if (g.M <= 256) {
+      launch_tiled<EPI, 256, 256, 4, 2, 2, 64>(g, s);
     } else {
-      GemmArgs h = g;
-      h.pick_rows = 320;
-      launch_tiled<EPI, 256, 256, 4, 2, 2, 64>(h, s);
-      if (g.M > 256) {
-        h.pick_rows = 256;
-        launch_tiled<EPI, 256, 320, 4, 2, 2, 64, true>(h, s);
-      }
+      // grid for 256-row tiles over the host bound (the larger of the two tilings)
+      const int per = ((g.N / 256) * ((g.M + 255) / 256) + 7) / 8;
+      hipLaunchKernelGGL(k_gemm_head_rows, dim3(8 * per), dim3(512), 0, s, g);
     }
   } else if (gemm_ksplit(g.M, g.N, g.K) > 1) {
     if (!g.kpart) return hipErrorInvalidValue;
