@@ -82,10 +82,10 @@ class HipEvents:
 
 
 def kernel_source_hash() -> str:
-    """Hash of the GEMM sources without comments and whitespace: the traffic
+    """Hash of the kernel sources without comments and whitespace: a counter
     record stays valid across comment-only edits, not across code changes."""
     h = hashlib.sha256()
-    for f in ("k_gemm.hip", "dlm_device.h", "dlm_internal.h"):
+    for f in ("k_gemm.hip", "k_attention.hip", "k_small.hip", "dlm_device.h", "dlm_internal.h"):
         text = open(os.path.join(ROOT, "masked_block_diffusion_denoise_amd", "csrc", f)).read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
         text = re.sub(r"//[^\n]*", "", text)
@@ -93,16 +93,19 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "kernel_counters.json")
+
+
 def traffic_for(kernel: str, batch: int):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if taken on the current kernel source."""
-    p = os.path.join(ROOT, "profiles", "lm_head_traffic.json")
-    if not os.path.exists(p):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled by a copy of known
+    size) from the committed counter record, if taken on the current kernel source."""
+    if not os.path.exists(COUNTERS_FILE):
         return None
     try:
-        rec = json.load(open(p))
+        rec = json.load(open(COUNTERS_FILE))
         if rec.get("source_hash") != kernel_source_hash():
             return None
-        return rec.get("per_launch_bytes", {}).get(f"{kernel}_b{batch}")
+        return rec.get("kernels", {}).get(f"{kernel}_b{batch}", {}).get("hbm_bytes")
     except Exception:
         return None
 
@@ -110,14 +113,6 @@ def traffic_for(kernel: str, batch: int):
 TIMERS = {"lm_head": 0, "attention": 1, "gate_up": 2, "down": 3, "qkv": 4, "o_proj": 5, "final_norm": 6}
 ROTATE = 3   # weight/KV copies the single-layer steps rotate over
 
-# LM-head launches in a counter run, told apart from the other GEMMs by the
-# head epilogue's template argument and the tile (k_gemm_tiled<EPI, BN, BM, ...>,
-# EPI_HEAD = 3).  At batch 32 one head is two launches, 256-row and up-to-320-row
-# tiles, of which only one does the work (the other reads the row count and
-# exits); a head's bytes are the sum of the two.  Batch 1: 256 x 32 (up to 32 rows) or
-# 256 x 64 tiles.
-HEAD_KERNELS = {"lm_head_b32": [re.compile(r"k_gemm_tiled<3, 256, 256,"), re.compile(r"k_gemm_tiled<3, 256, 320,")],
-                "lm_head_b1": [re.compile(r"k_gemm_tiled<3, 256, (32|64),")]}
 COPY_KERNEL = re.compile(r"copyBuffer")
 
 
@@ -134,41 +129,99 @@ def copy_probe(mib: int) -> None:
     del src, dst
 
 
-def _counter_means(d: str, counter: str) -> dict:
-    """Mean per-dispatch value of `counter` for each kernel name in a rocprofv3 csv directory."""
+# The libdlm launches of one denoise step in order, labelled by position: the
+# k-th tiled GEMM of a step is QKV, O, gate/up, down (the head is told apart by
+# its epilogue argument, EPI_HEAD = 3, or its own kernel).
+_GEMM_ORDER = ("qkv", "o_proj", "gate_up", "down")
+_NAMED = [("k_embed_norm", "embed_norm"), ("k_rope_kv", "rope_kv"), ("k_attn_merge", "attention_merge"),
+          ("k_attn<", "attention"), ("k_resid_norm", "resid_norm"), ("k_rmsnorm", "rmsnorm"),
+          ("k_splitk_reduce", "splitk_reduce"), ("k_masked_norm", "final_norm"), ("k_head_merge", "head_merge"),
+          ("k_commit", "commit"), ("k_gemm_head_rows", "lm_head"), ("k_gemm_tiled<3,", "lm_head")]
+
+
+def label_steps(dispatches):
+    """[(kernel name, grid size, {counter: value})] in dispatch order -> per-step
+    lists of (label, values); a step starts at the embedding kernel.  The
+    residual norm after O is 'o_norm', after down 'down_norm'; the reduction
+    after gate/up is 'gate_up_reduce'.  The batch of a step is the final norm's
+    grid (one 256-thread workgroup per canvas row, 32 rows per sequence)."""
+    steps, cur, ngemm = [], None, 0
+    for name, grid, vals in dispatches:
+        if "dlm::" not in name:
+            continue
+        if "k_embed_norm" in name:
+            cur = {"items": [], "batch": None}
+            steps.append(cur)
+            ngemm = 0
+        if cur is None:
+            continue
+        lab = None
+        for pat, l in _NAMED:
+            if pat in name:
+                lab = l
+                break
+        if lab is None and "k_gemm_tiled<" in name:
+            lab = _GEMM_ORDER[ngemm] if ngemm < len(_GEMM_ORDER) else "gemm"
+            ngemm += 1
+        if lab in ("resid_norm", "rmsnorm"):
+            lab = "o_norm" if ngemm <= 2 else "down_norm"
+        if lab == "splitk_reduce":
+            lab = "gate_up_reduce"
+        if lab == "final_norm" and grid:
+            cur["batch"] = max(1, grid // 256 // 32)
+        cur["items"].append((lab or name, vals))
+    return steps
+
+
+def _read_counters(dirs):
+    """Dispatches of rocprofv3 counter-collection csv files: {dispatch id: [name, grid, {counter: value}]}."""
     import csv
     import glob
-    vals: dict = {}
-    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
-        for row in csv.DictReader(open(f)):
-            if row["Counter_Name"] != counter:
-                continue
-            vals.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
-    return vals
+    d = {}
+    for base in dirs:
+        for f in glob.glob(os.path.join(base, "**", "*counter_collection.csv"), recursive=True):
+            for row in csv.DictReader(open(f)):
+                key = (base, int(row["Dispatch_Id"]))
+                rec = d.setdefault(key, [row["Kernel_Name"], int(float(row.get("Grid_Size", 0) or 0)), {}])
+                rec[2][row["Counter_Name"]] = rec[2].get(row["Counter_Name"], 0.0) + float(row["Counter_Value"])
+    return d
 
 
-def traffic_from(fetch_dir: str, write_dir: str, copy_mib: int, command: str) -> dict:
-    """Per-launch HBM bytes of the LM head from a FETCH_SIZE run and a WRITE_SIZE run,
-    each scaled by what the counter read for the copy probe (known bytes / counter bytes)."""
+def counters_from(dirs, copy_mib: int, command: str) -> dict:
+    """Per-kernel counter means from rocprofv3 --pmc runs of `bench.py --no-e2e
+    --copy-probe-mib N` (one run per counter group), labelled by position in
+    the step and batch.  FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled
+    by what each read for the copy probe of known size; hbm_bytes is their sum."""
     out = {"source_hash": kernel_source_hash(), "command": command, "copy_probe_bytes": copy_mib << 20,
-           "per_launch_bytes": {}, "raw_kib": {}}
-    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
-        vals = _counter_means(d, counter)
-        copies = [max(v) for k, v in vals.items() if COPY_KERNEL.search(k)]
-        if not copies:
-            raise SystemExit(f"no copy dispatch with {counter} in {d}")
-        scale = (copy_mib << 20) / (max(copies) * 1024.0)
-        out[f"{counter.lower()}_scale"] = round(scale, 4)
-        for key, pats in HEAD_KERNELS.items():
-            kib = 0.0
-            for pat in pats:
-                launches = [x for k, v in vals.items() if pat.search(k) for x in v]
-                if launches:
-                    kib += sum(launches) / len(launches)
-            if kib == 0.0:
+           "scale": {}, "kernels": {}}
+    agg = {}
+    for base in dirs:
+        disp = _read_counters([base])
+        order = sorted(disp.items(), key=lambda kv: kv[0][1])
+        for name, grid, vals in (v for _, v in order):
+            if COPY_KERNEL.search(name):
+                for c, x in vals.items():
+                    if c in ("FETCH_SIZE", "WRITE_SIZE"):
+                        out["scale"][c] = max(out["scale"].get(c, 0.0), x)
+        for st in label_steps([v for _, v in order]):
+            if not st["batch"]:
                 continue
-            out["raw_kib"][f"{key}_{counter}"] = round(kib, 1)
-            out["per_launch_bytes"][key] = out["per_launch_bytes"].get(key, 0) + round(kib * 1024.0 * scale)
+            for lab, vals in st["items"]:
+                rec = agg.setdefault(f"{lab}_b{st['batch']}", {})
+                for c, x in vals.items():
+                    rec.setdefault(c, []).append(x)
+    for c in list(out["scale"]):
+        out["scale"][c] = round((copy_mib << 20) / (out["scale"][c] * 1024.0), 4)
+    for key, rec in sorted(agg.items()):
+        k = {c: round(sum(v) / len(v), 1) for c, v in rec.items()}
+        k["dispatches"] = max(len(v) for v in rec.values())
+        by = 0.0
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            if c in k and c in out["scale"]:
+                by += k[c] * 1024.0 * out["scale"][c]
+        if by:
+            k["hbm_bytes"] = round(by)
+        out["kernels"][key] = k
     return out
 
 
@@ -181,7 +234,7 @@ class ClockSampler:
     """Samples the GPU's current shader clock (sysfs pp_dpm_sclk, the '*' level)
     in a thread while the timed steps run; no-op where sysfs is not readable."""
 
-    def __init__(self, period_s=0.02):
+    def __init__(self, period_s=0.002):
         import glob
         import threading
         self.paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
@@ -227,7 +280,9 @@ class ClockSampler:
 
 def gpu_info() -> dict:
     import torch
-    out = {"device": torch.cuda.get_device_name(0), "hip_runtime": torch.version.hip}
+    props = torch.cuda.get_device_properties(0)
+    out = {"device": torch.cuda.get_device_name(0) or getattr(props, "gcnArchName", ""),
+           "compute_units": props.multi_processor_count, "hip_runtime": torch.version.hip}
     try:
         out["rocm"] = open("/opt/rocm/.info/version").read().strip()
     except OSError:
@@ -688,16 +743,16 @@ def main(argv=None) -> int:
     ap.add_argument("--batches", default="32,1", help="batch sizes; the first is the headline")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run a plain copy of this many MiB first (scale for counter runs)")
-    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="no GPU: digest two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
-                         "`bench.py --copy-probe-mib N` into profiles/lm_head_traffic.json")
-    ap.add_argument("--traffic-command", default="", help="the counter command, recorded with --traffic-from")
+    ap.add_argument("--counters-from", nargs="+", metavar="DIR",
+                    help="no GPU: digest rocprofv3 --pmc runs of `bench.py --no-e2e --copy-probe-mib N` (one "
+                         "directory per counter group) into profiles/kernel_counters.json")
+    ap.add_argument("--counters-command", default="", help="the counter commands, recorded with --counters-from")
     a = ap.parse_args(argv)
-    if a.traffic_from:
-        rec = traffic_from(a.traffic_from[0], a.traffic_from[1], a.copy_probe_mib or 1024, a.traffic_command)
-        with open(os.path.join(ROOT, "profiles", "lm_head_traffic.json"), "w") as f:
+    if a.counters_from:
+        rec = counters_from(a.counters_from, a.copy_probe_mib or 1024, a.counters_command)
+        with open(COUNTERS_FILE, "w") as f:
             json.dump(rec, f, indent=1)
-        print(json.dumps(rec))
+        print(json.dumps(rec)[:2000])
         return 0
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: libdlm has no multi-GPU path (batch rows would shard across "

@@ -52,3 +52,51 @@ def test_bench_line_has_the_contract_fields():
     assert line["single_layer_step_committed_tokens_per_s"] == 32 * 800.0
     assert set(line["step_ms"]) >= {"median", "p10", "p90", "one_copy_wall_mean"}
     assert "b1" in line and "down_with_final_norm" in line["b1"]["kernels"]
+
+
+def test_counter_digest_labels_each_kernel_of_a_step(tmp_path):
+    """The counter digest on a made-up rocprofv3 counter csv: dispatches are
+    labelled by their place in the step, the batch comes from the final norm's
+    grid, and FETCH_SIZE is scaled by what it read for the 1 GiB copy."""
+    import csv
+    import bench
+    b32 = ["void dlm::k_embed_norm<512>(int const*)", "void dlm::k_gemm_tiled<0, 192, 128, 2, 2, 2, 64, false>(x)",
+           "void dlm::k_rope_kv<false>(x)", "void dlm::k_attn<128, 4, true>(x)",
+           "void dlm::k_gemm_tiled<1, 128, 128, 2, 2, 2, 64, false>(x)", "dlm::k_rmsnorm(float const*)",
+           "void dlm::k_gemm_tiled<2, 256, 256, 4, 2, 2, 64, false>(x)",
+           "void dlm::k_gemm_tiled<4, 256, 256, 4, 2, 2, 64, false>(x)", "dlm::k_masked_norm(x)",
+           "dlm::k_gemm_head_rows(dlm::GemmArgs)", "dlm::k_head_merge(x)", "dlm::k_commit(x)"]
+    b1 = ["void dlm::k_embed_norm<512>(int const*)", "void dlm::k_gemm_tiled<4, 128, 64, 4, 1, 3, 64, false>(x)",
+          "void dlm::k_rope_kv<true>(x)", "void dlm::k_attn<128, 4, false>(x)", "void dlm::k_attn_merge<128>(x)",
+          "void dlm::k_gemm_tiled<4, 128, 64, 4, 1, 3, 64, false>(x)", "void dlm::k_resid_norm<512>(x)",
+          "void dlm::k_gemm_tiled<4, 256, 64, 4, 1, 2, 64, false>(x)", "void dlm::k_splitk_reduce<2>(x)",
+          "void dlm::k_gemm_tiled<4, 128, 64, 4, 1, 3, 64, false>(x)", "dlm::k_masked_norm(x)",
+          "void dlm::k_gemm_tiled<3, 256, 32, 4, 1, 2, 64, false>(x)", "dlm::k_head_merge(x)", "dlm::k_commit(x)"]
+    rows, did = [], 0
+
+    def add(name, grid, kib):
+        nonlocal did
+        did += 1
+        rows.append({"Dispatch_Id": did, "Kernel_Name": name, "Grid_Size": grid, "Counter_Name": "FETCH_SIZE",
+                     "Counter_Value": kib})
+    add("__amd_rocclr_copyBuffer", 4096, 524288.0)
+    for _ in range(2):
+        for i, n in enumerate(b32):
+            add(n, 1024 * 256 if "masked_norm" in n else 256, 100.0 + i)
+    for i, n in enumerate(b1):
+        add(n, 32 * 256 if "masked_norm" in n else 256, 10.0 + i)
+    d = tmp_path / "pmc_fetch" / "x"
+    d.mkdir(parents=True)
+    with open(d / "run_counter_collection.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=list(rows[0]))
+        w.writeheader()
+        w.writerows(rows)
+    rec = bench.counters_from([str(tmp_path / "pmc_fetch")], 1024, "cmd")
+    k = rec["kernels"]
+    assert rec["scale"]["FETCH_SIZE"] == 2.0
+    assert k["qkv_b32"]["FETCH_SIZE"] == 101.0 and k["qkv_b32"]["dispatches"] == 2
+    assert k["lm_head_b32"]["FETCH_SIZE"] == 109.0 and k["down_b32"]["FETCH_SIZE"] == 107.0
+    assert k["o_norm_b32"]["FETCH_SIZE"] == 105.0 and k["gate_up_b32"]["FETCH_SIZE"] == 106.0
+    assert k["attention_merge_b1"]["FETCH_SIZE"] == 14.0 and k["o_norm_b1"]["FETCH_SIZE"] == 16.0
+    assert k["gate_up_reduce_b1"]["FETCH_SIZE"] == 18.0 and k["down_b1"]["FETCH_SIZE"] == 19.0
+    assert k["lm_head_b1"]["hbm_bytes"] == round(21.0 * 1024 * 2.0)
