@@ -37,6 +37,10 @@ struct GemmArgs {
   // K-split (set by gemm() when gemm_ksplit() > 1): fp32 [ksplit][M][N] partials
   float* kpart;         // workspace of gemm_workspace_bytes(M, N, K) bytes, from the caller
   int ksplit;
+  // tile order: 0 = row tiles fastest, then K ranges, then weight tiles (the
+  // workgroups sharing a weight tile share an XCD's L2); 1 = weight tiles
+  // fastest, then row tiles, then K ranges (set for long-K split products)
+  int weights_fastest = 0;
 };
 
 int gemm_head_tile_n(int M);                       // vocab columns per EPI_HEAD partial
