@@ -33,8 +33,9 @@ SHAPES = [(16, 256, 128), (13, 1024, 512), (32, 6144, 4096), (64, 384, 256), (32
           (1000, 5120, 256),
           # at most one 128 x 128 tile per CU, several row tiles (ragged rows)
           (1000, 2048, 256),
-          # at least one 256 x 256 tile per CU: one 64-deep stage, two (ragged rows)
-          (520, 32768, 64), (520, 32768, 128),
+          # at least one 256 x 256 tile per CU: one 64-deep stage, two, three (ragged rows; the last
+          # row tile's second wavefront row is idle), the split ring's activation buffers reused
+          (520, 32768, 64), (520, 32768, 128), (520, 32768, 192), (264, 65536, 512),
           # long K over few 256 x 256 tiles: K split into 8 parts of 16 stages
           (300, 1024, 8192)]
 

@@ -63,7 +63,10 @@ def check(R, V, d, mask_id, seed, planted=True, with_logits=True):
                                            # full 256-row tiles only / 64-row remainder tiles only / both
                                            (256, 2048, 256, 9), (100, 2048, 256, 3), (577, 1024, 128, 1),
                                            # rows split evenly over 3 tiles of up to 320 / four 256-row tiles
-                                           (900, 1024, 128, 7), (1000, 1024, 128, 3)])
+                                           (900, 1024, 128, 7), (1000, 1024, 128, 3),
+                                           # 256-row tiles: ragged second tile over eight stages, one
+                                           # partly live tile over three
+                                           (496, 2048, 512, 11), (200, 2048, 192, 4)])
 def test_lm_head_small(R, V, d, mask_id):
     announce(f"lm head R={R} V={V} d={d}")
     c = check(R, V, d, mask_id, seed=R)
