@@ -384,8 +384,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* lds) {
     // 3-deep ring at [2 HALF, 5 HALF).  So one wavefront of a SIMD multiplies
     // while the other loads.  The products of each 16-deep step are issued with
     // the next step's fragment reads in flight (step_2_4).  Batch-32 gate/up
-    // (1024 x 28672 x 4096): 271 -> 234 us; LM head, 496 rows: 560 -> 526 us;
-    // down (K split): 142 -> 130 us.
+    // (1024 x 28672 x 4096): 0.257 -> 0.231 ms; LM head, 496 rows: 0.535 ->
+    // 0.479 ms; down (K split): 0.126 -> 0.115 ms.
     constexpr int HALF = BN * ROW;
     static_assert(BLK == 8 && 4 * BLK * 1024 == HALF, "wavefronts 0-3 load exactly the weight half");
     static_assert(TN == 2 && TM == 4, "step_2_4 wavefront tiles");
