@@ -431,35 +431,35 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* lds) {
     }
   } else {
 #pragma unroll
-  for (int p = 0; p < NBUF - 1; ++p)
-    if (p < nk) issue(p);
-  for (int kt = 0; kt < nk; ++kt) {
-    // stage kt has landed once at most the later stages' loads are outstanding
-    const int later = min(nk - 1 - kt, NBUF - 2);
-    if (later >= 4)
-      wait_vm_barrier<4 * BLK>();
-    else if (later == 3)
-      wait_vm_barrier<3 * BLK>();
-    else if (later == 2)
-      wait_vm_barrier<2 * BLK>();
-    else if (later == 1)
-      wait_vm_barrier<BLK>();
-    else
-      wait_vm_barrier<0>();
-    if (kt + NBUF - 1 < nk) issue(kt + NBUF - 1);
-    if (live == 0) continue;
-    const uint32_t sb = lbase + (kt % NBUF) * STAGE;
+    for (int p = 0; p < NBUF - 1; ++p)
+      if (p < nk) issue(p);
+    for (int kt = 0; kt < nk; ++kt) {
+      // stage kt has landed once at most the later stages' loads are outstanding
+      const int later = min(nk - 1 - kt, NBUF - 2);
+      if (later >= 4)
+        wait_vm_barrier<4 * BLK>();
+      else if (later == 3)
+        wait_vm_barrier<3 * BLK>();
+      else if (later == 2)
+        wait_vm_barrier<2 * BLK>();
+      else if (later == 1)
+        wait_vm_barrier<BLK>();
+      else
+        wait_vm_barrier<0>();
+      if (kt + NBUF - 1 < nk) issue(kt + NBUF - 1);
+      if (live == 0) continue;
+      const uint32_t sb = lbase + (kt % NBUF) * STAGE;
 #pragma unroll
-    for (int s = 0; s < NSTEP; ++s) {
-      u32x4 fa[TN], fb[TM];
-      lds_frags<TN, TM, 32 * ROW>(sb + fa_off[s], sb + fb_off[s], fa, fb);
+      for (int s = 0; s < NSTEP; ++s) {
+        u32x4 fa[TN], fb[TM];
+        lds_frags<TN, TM, 32 * ROW>(sb + fa_off[s], sb + fb_off[s], fa, fb);
 #pragma unroll
-      for (int i = 0; i < TN; ++i)
+        for (int i = 0; i < TN; ++i)
 #pragma unroll
-        for (int j = 0; j < TM; ++j)
-          if (j < live) acc[i][j] = mfma32x32x16(as_bf16x8(fa[i]), as_bf16x8(fb[j]), acc[i][j]);
+          for (int j = 0; j < TM; ++j)
+            if (j < live) acc[i][j] = mfma32x32x16(as_bf16x8(fa[i]), as_bf16x8(fb[j]), acc[i][j]);
+      }
     }
-  }
   }
 
   // lane holds D[n][m]: m = m0 + (wm*TM + j)*32 + (lane&31),
