@@ -243,6 +243,67 @@ __device__ __forceinline__ void step_2_4(uint32_t a, uint32_t b, const u32x4 (&f
       : "memory");
 }
 
+// The same for the 3 x 2 and 2 x 2 wavefront tiles of the 4-wavefront tiles.
+template <int D>
+__device__ __forceinline__ void step_3_2(uint32_t a, uint32_t b, const u32x4 (&fa)[3], const u32x4 (&fb)[2],
+                                         u32x4 (&na)[3], u32x4 (&nb)[2], f32x16 (&acc)[3][2]) {
+  asm volatile(
+      "ds_read_b128 %6, %16\n\t"
+      "ds_read_b128 %7, %16 offset:%18\n\t"
+      "ds_read_b128 %8, %16 offset:%19\n\t"
+      "ds_read_b128 %9, %17\n\t"
+      "ds_read_b128 %10, %17 offset:%18\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %11, %14, %0\n\t"
+      "v_mfma_f32_32x32x16_bf16 %1, %11, %15, %1\n\t"
+      "v_mfma_f32_32x32x16_bf16 %2, %12, %14, %2\n\t"
+      "v_mfma_f32_32x32x16_bf16 %3, %12, %15, %3\n\t"
+      "v_mfma_f32_32x32x16_bf16 %4, %13, %14, %4\n\t"
+      "v_mfma_f32_32x32x16_bf16 %5, %13, %15, %5\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[1][0]), "+v"(acc[1][1]), "+v"(acc[2][0]), "+v"(acc[2][1]),
+        "=&v"(na[0]), "=&v"(na[1]), "=&v"(na[2]), "=&v"(nb[0]), "=&v"(nb[1])
+      : "v"(fa[0]), "v"(fa[1]), "v"(fa[2]), "v"(fb[0]), "v"(fb[1]), "v"(a), "v"(b), "i"(D), "i"(2 * D)
+      : "memory");
+}
+
+template <int D>
+__device__ __forceinline__ void step_2_2(uint32_t a, uint32_t b, const u32x4 (&fa)[2], const u32x4 (&fb)[2],
+                                         u32x4 (&na)[2], u32x4 (&nb)[2], f32x16 (&acc)[2][2]) {
+  asm volatile(
+      "ds_read_b128 %4, %12\n\t"
+      "ds_read_b128 %5, %12 offset:%14\n\t"
+      "ds_read_b128 %6, %13\n\t"
+      "ds_read_b128 %7, %13 offset:%14\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %8, %10, %0\n\t"
+      "v_mfma_f32_32x32x16_bf16 %1, %8, %11, %1\n\t"
+      "v_mfma_f32_32x32x16_bf16 %2, %9, %10, %2\n\t"
+      "v_mfma_f32_32x32x16_bf16 %3, %9, %11, %3\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[1][0]), "+v"(acc[1][1]), "=&v"(na[0]), "=&v"(na[1]),
+        "=&v"(nb[0]), "=&v"(nb[1])
+      : "v"(fa[0]), "v"(fa[1]), "v"(fb[0]), "v"(fb[1]), "v"(a), "v"(b), "i"(D)
+      : "memory");
+}
+
+template <int TN, int TM, int D>
+__device__ __forceinline__ void step_pipe(uint32_t a, uint32_t b, const u32x4 (&fa)[TN], const u32x4 (&fb)[TM],
+                                          u32x4 (&na)[TN], u32x4 (&nb)[TM], f32x16 (&acc)[TN][TM]) {
+  if constexpr (TN == 3 && TM == 2)
+    step_3_2<D>(a, b, fa, fb, na, nb, acc);
+  else if constexpr (TN == 2 && TM == 2)
+    step_2_2<D>(a, b, fa, fb, na, nb, acc);
+  else
+    static_assert(TN < 0, "no pipelined step for this wavefront tile");
+}
+
+// The 4-wavefront tiles with 128 or more rows (one wavefront per SIMD) run a
+// pipelined ring (see gemm_tile) wherever all of a wavefront's fragments are
+// live.
+template <int T, int BM, int TN, int TM>
+constexpr bool pipe_ring() {
+  return T == 256 && BM >= 128 && ((TN == 3 && TM == 2) || (TN == 2 && TM == 2));
+}
+
 // The 8-wavefront 256 x 256 tiles with 64-deep stages run a split ring (see
 // gemm_tile): weights in two 32 KB buffers, activations in three.
 template <int T, int BN, int BM, int NBUF, int BK>
@@ -364,6 +425,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* lds) {
   }
   const uint32_t lbase = lds_addr(lds);
   constexpr bool SPLIT = split_ring<T, BN, BM, NBUF, BK>();
+  constexpr bool PIPE = pipe_ring<T, BM, TN, TM>();
   // Activation fragments (32 rows each) past the live rows (the ragged last row
   // tile, e.g. the masked rows of the LM head) are not multiplied; a wavefront
   // with none left still loads its share of every stage and joins every
@@ -430,35 +492,94 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* lds) {
       if (!early && kt + 2 < nk) issue_half(kt + 2);
     }
   } else {
+    // Plain ring: every wavefront issues its share of stage kt + NBUF - 1 right
+    // after the barrier, then multiplies stage kt step by step.
+    auto plain_ring = [&]() {
 #pragma unroll
-    for (int p = 0; p < NBUF - 1; ++p)
-      if (p < nk) issue(p);
-    for (int kt = 0; kt < nk; ++kt) {
-      // stage kt has landed once at most the later stages' loads are outstanding
-      const int later = min(nk - 1 - kt, NBUF - 2);
-      if (later >= 4)
-        wait_vm_barrier<4 * BLK>();
-      else if (later == 3)
-        wait_vm_barrier<3 * BLK>();
-      else if (later == 2)
-        wait_vm_barrier<2 * BLK>();
-      else if (later == 1)
-        wait_vm_barrier<BLK>();
-      else
-        wait_vm_barrier<0>();
-      if (kt + NBUF - 1 < nk) issue(kt + NBUF - 1);
-      if (live == 0) continue;
-      const uint32_t sb = lbase + (kt % NBUF) * STAGE;
+      for (int p = 0; p < NBUF - 1; ++p)
+        if (p < nk) issue(p);
+      for (int kt = 0; kt < nk; ++kt) {
+        // stage kt has landed once at most the later stages' loads are outstanding
+        const int later = min(nk - 1 - kt, NBUF - 2);
+        if (later >= 4)
+          wait_vm_barrier<4 * BLK>();
+        else if (later == 3)
+          wait_vm_barrier<3 * BLK>();
+        else if (later == 2)
+          wait_vm_barrier<2 * BLK>();
+        else if (later == 1)
+          wait_vm_barrier<BLK>();
+        else
+          wait_vm_barrier<0>();
+        if (kt + NBUF - 1 < nk) issue(kt + NBUF - 1);
+        if (live == 0) continue;
+        const uint32_t sb = lbase + (kt % NBUF) * STAGE;
 #pragma unroll
-      for (int s = 0; s < NSTEP; ++s) {
-        u32x4 fa[TN], fb[TM];
-        lds_frags<TN, TM, 32 * ROW>(sb + fa_off[s], sb + fb_off[s], fa, fb);
+        for (int s = 0; s < NSTEP; ++s) {
+          u32x4 fa[TN], fb[TM];
+          lds_frags<TN, TM, 32 * ROW>(sb + fa_off[s], sb + fb_off[s], fa, fb);
 #pragma unroll
-        for (int i = 0; i < TN; ++i)
+          for (int i = 0; i < TN; ++i)
 #pragma unroll
-          for (int j = 0; j < TM; ++j)
-            if (j < live) acc[i][j] = mfma32x32x16(as_bf16x8(fa[i]), as_bf16x8(fb[j]), acc[i][j]);
+            for (int j = 0; j < TM; ++j)
+              if (j < live) acc[i][j] = mfma32x32x16(as_bf16x8(fa[i]), as_bf16x8(fb[j]), acc[i][j]);
+        }
       }
+    };
+    if constexpr (PIPE) {
+      static_assert(NBUF <= 4, "wait ladder of the pipelined ring covers two later stages");
+      if (live == TM) {
+        // Pipelined ring (one wavefront per SIMD, so nothing else on the SIMD
+        // fills its stalls): each 16-deep step's products run with the next
+        // step's fragment reads in flight (step_pipe), and the wavefront's
+        // share of stage kt + NBUF - 1 is issued in pieces after each step's
+        // products instead of all at once after the barrier.  With three
+        // buffers (two stages in flight) on the batch-32 QKV (1024 x 6144 x
+        // 4096, 192 x 128 tiles) and O (1024 x 4096 x 4096, 128 x 128) products:
+        // 68.6 -> 62.7 us and 54.2 -> 50.8 us.
+#pragma unroll
+        for (int p = 0; p < NBUF - 1; ++p)
+          if (p < nk) issue(p);
+        for (int kt = 0; kt < nk; ++kt) {
+          const int later = min(nk - 1 - kt, NBUF - 2);
+          if (later >= 2)
+            wait_vm_barrier<2 * BLK>();
+          else if (later == 1)
+            wait_vm_barrier<BLK>();
+          else
+            wait_vm_barrier<0>();
+          const bool more = kt + NBUF - 1 < nk;
+          uint8_t* dst = lds + ((kt + NBUF - 1) % NBUF) * STAGE + w * BLK * 1024;
+          const int koff = (k_lo + kt + NBUF - 1) * BK;
+          const uint32_t sb = lbase + (kt % NBUF) * STAGE;
+          u32x4 fa[TN], fb[TM];
+          lds_frags<TN, TM, 32 * ROW>(sb + fa_off[0], sb + fb_off[0], fa, fb);
+#pragma unroll
+          for (int s = 0; s < NSTEP; ++s) {
+            if (s + 1 < NSTEP) {
+              u32x4 na[TN], nb[TM];
+              step_pipe<TN, TM, 32 * ROW>(sb + fa_off[s + 1], sb + fb_off[s + 1], fa, fb, na, nb, acc);
+#pragma unroll
+              for (int i = 0; i < TN; ++i) fa[i] = na[i];
+#pragma unroll
+              for (int j = 0; j < TM; ++j) fb[j] = nb[j];
+            } else {
+#pragma unroll
+              for (int i = 0; i < TN; ++i)
+#pragma unroll
+                for (int j = 0; j < TM; ++j) acc[i][j] = mfma32x32x16(as_bf16x8(fa[i]), as_bf16x8(fb[j]), acc[i][j]);
+            }
+            if (more) {
+#pragma unroll
+              for (int b = s * BLK / NSTEP; b < (s + 1) * BLK / NSTEP; ++b) load_lds16(src[b] + koff, dst + b * 1024);
+            }
+          }
+        }
+      } else {
+        plain_ring();
+      }
+    } else {
+      plain_ring();
     }
   }
 
@@ -784,11 +905,11 @@ static hipError_t launch_epi(const GemmArgs& g, hipStream_t s) {
     if (g.N % 256 == 0 && (g.N / 256) * ((g.M + 255) / 256) >= 256)
       launch_tiled<EPI, 256, 256, 4, 2, 2, 64>(g, s);
     else if (t128 <= 256 && g.M > 128)  // several row tiles: MFMA-bound (O at 1024 rows 55 -> 52 us)
-      launch_tiled<EPI, 128, 128, 2, 2, 2, 64>(g, s);
+      launch_tiled<EPI, 128, 128, 2, 2, 3, 64>(g, s);
     else if (t128 <= 256)  // one row tile: HBM-bound, deeper ring (gate/up at 128 rows: 58 vs 74 us)
       launch_tiled<EPI, 128, 128, 2, 2, 3, 64>(g, s);
     else if (g.N % 192 == 0 && (g.N / 192) * ((g.M + 127) / 128) <= 256)
-      launch_tiled<EPI, 192, 128, 2, 2, 2, 64>(g, s);
+      launch_tiled<EPI, 192, 128, 2, 2, 3, 64>(g, s);
     else if (g.N % 256 == 0)
       launch_tiled<EPI, 256, 128, 4, 2, 3>(g, s);
     else
