@@ -20,9 +20,12 @@
 // index fastest ([cap/16][hd][16]).  So the V operand is one 16-byte LDS read per
 // MFMA and no transpose is needed anywhere.
 //
-// K/V tiles stream through a ring of two LDS stages of two tiles each, filled
-// by direct global-to-LDS loads (global_load_lds_dwordx4): one stage is in
-// flight while the other is used, one wait + barrier per stage.  The two tiles
+// K/V tiles stream through a ring of LDS stages of two tiles each, filled by
+// direct global-to-LDS loads (global_load_lds_dwordx4), one wait + barrier per
+// stage: two stages (one in flight), or three (two in flight) for long key
+// ranges with one workgroup per CU.  With SPR a stage's loads are issued one
+// tile at a time between the batches of the S product rather than all at once
+// after the barrier.  The two tiles
 // of a stage are computed together (one softmax update over 64 keys), which
 // gives each wavefront independent MFMA chains to overlap -- with one or two
 // wavefronts per SIMD, a single tile's dependent chain (S product, softmax,
@@ -48,7 +51,7 @@ constexpr int MIN_CHUNK = 128;
 // batch 4 over a 65536-position prefix, and no faster at batch 1); key splits
 // are only made for that second workgroup while they stay long (attn_splits).
 constexpr int TARGET_WG = 512;
-constexpr int SUB = 2;  // 32-key tiles per ring stage (two stages in the ring)
+constexpr int SUB = 2;  // 32-key tiles per ring stage
 constexpr float RESCALE = 8.f;  // lazy-rescale threshold (log2 units)
 
 __device__ __forceinline__ uint32_t att_lds_addr(const void* p) {
@@ -120,7 +123,7 @@ __device__ __forceinline__ void lds_read_n<2>(const uint32_t (&a)[2], u32x4 (&f)
                : "memory");
 }
 
-template <int HD, int GS, bool NT>
+template <int HD, int GS, bool NT, int NB, bool SPR>
 __global__ void __launch_bounds__(GS * 64) k_attn(AttnArgs a, int chunk_len) {
   constexpr int KCH = HD / 8;              // 16-byte chunks per key row
   constexpr int TILE_K = KT * HD * 2;      // bytes of a K tile (= bytes of a V tile)
@@ -130,7 +133,8 @@ __global__ void __launch_bounds__(GS * 64) k_attn(AttnArgs a, int chunk_len) {
   static_assert((TILE / 1024) % GS == 0 && TBLK >= 1, "a tile must split evenly over the wavefronts");
   constexpr int NS = HD / 16;              // 16-deep steps of the S product
   constexpr int ND = HD / 32;              // 32-row blocks of the output
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE];
+  static_assert(NB == 2 || NB == 3, "two or three ring stages");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NB * STAGE];
 
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int split = blockIdx.x, qb = blockIdx.y;
@@ -192,14 +196,12 @@ __global__ void __launch_bounds__(GS * 64) k_attn(AttnArgs a, int chunk_len) {
       src[i] = vc + vrow * 16 + (ph ^ vxor(vrow)) * 8;
     }
   }
-  // stage st: tiles st*SUB .. st*SUB+SUB-1 of this workgroup's key range; a tile
+  // tile u of stage st: tile st*SUB + u of this workgroup's key range; a tile
   // past the range is not loaded (its keys are masked and its values zeroed)
-  auto issue = [&](int st) {
-#pragma unroll
-    for (int u = 0; u < SUB; ++u) {
-      const int t = st * SUB + u;
-      if (t >= ntiles) break;
-      uint8_t* dst = lds + (st & 1) * STAGE + u * TILE + w * TBLK * 1024;
+  auto issue_tile = [&](int st, int u) {
+    const int t = st * SUB + u;
+    if (t < ntiles) {
+      uint8_t* dst = lds + (st % NB) * STAGE + u * TILE + w * TBLK * 1024;
       const size_t off = static_cast<size_t>(kbeg + t * KT) * HD;
 #pragma unroll
       for (int i = 0; i < TBLK; ++i) att_load_lds16<NT>(src[i] + off, dst + i * 1024);
@@ -216,21 +218,37 @@ __global__ void __launch_bounds__(GS * 64) k_attn(AttnArgs a, int chunk_len) {
   const uint32_t voff = TILE_K + ar * 32 + ((half ^ vxor(ar)) << 4);
   const uint32_t lbase = att_lds_addr(lds);
 
-  if (nst > 0) issue(0);
+#pragma unroll
+  for (int p = 0; p < NB - 1; ++p)
+#pragma unroll
+    for (int u = 0; u < SUB; ++u)
+      if (p < nst) issue_tile(p, u);
   for (int st = 0; st < nst; ++st) {
-    // two stages: stage st has landed once no load is outstanding; the barrier
-    // also retires stage st - 1, which the next issue refills
-    att_wait_barrier<0>();
-    if (st + 1 < nst) issue(st + 1);
+    // stage st has landed once at most stage st + 1's loads (three stages) are
+    // outstanding; the barrier also retires stage st - 1, whose buffer this
+    // stage refills with stage st + NB - 1
+    if (NB == 3 && st + 1 < nst) {
+      if (ntiles - (st + 1) * SUB >= SUB)
+        att_wait_barrier<SUB * TBLK>();
+      else
+        att_wait_barrier<TBLK>();
+    } else {
+      att_wait_barrier<0>();
+    }
+    const bool more = st + NB - 1 < nst;
+    if (!SPR && more) {
+#pragma unroll
+      for (int u = 0; u < SUB; ++u) issue_tile(st + NB - 1, u);
+    }
     const int k0 = kbeg + st * SUB * KT;
-    const uint32_t sb = lbase + (st & 1) * STAGE;
+    const uint32_t sb = lbase + (st % NB) * STAGE;
     // The stage that reaches past the range (the last one): cache slots past the
     // row's end may hold anything (also NaN), and a tile past the range was not
     // loaded, so their values are zeroed in LDS -- a zero probability alone
     // would still give 0 * NaN.  No load is in flight on the last stage.
     const bool tail = k0 + SUB * KT > kend;
     if (tail) {
-      uint8_t* st_lds = lds + (st & 1) * STAGE;
+      uint8_t* st_lds = lds + (st % NB) * STAGE;
       const int first = max(0, kend - k0);  // first stage key past the range
       for (int i = threadIdx.x; i < (SUB * KT - first) * HD; i += GS * 64) {
         const int kk = first + i / HD, d = i % HD;      // stage key, value dim
@@ -264,6 +282,12 @@ __global__ void __launch_bounds__(GS * 64) k_attn(AttnArgs a, int chunk_len) {
       for (int s = 0; s < KB; ++s)
 #pragma unroll
         for (int u = 0; u < SUB; ++u) sacc[u] = mfma32x32x16(as_bf16x8(kf[u * KB + s]), qf[hs + s], sacc[u]);
+      // one tile of stage st + NB - 1 after each batch of the S product
+      if (SPR && more && hs / KB < SUB) issue_tile(st + NB - 1, hs / KB);
+    }
+    if (SPR && more) {
+#pragma unroll
+      for (int u = NS / KB; u < SUB; ++u) issue_tile(st + NB - 1, u);
     }
     // register r of tile u holds key k0 + u*KT + 16*(r/8) + 8*half + (r%8).
     // Only the last stage of the range and causal passes need a mask.
@@ -477,10 +501,27 @@ static hipError_t launch(const AttnArgs& a, hipStream_t s) {
   // denoise steps of a block re-read the same prefix (batch 1 over 4096
   // positions, 17 MB, was slower with non-temporal loads).
   const double kv_bytes = 2.0 * a.B * a.G * static_cast<double>(a.max_kv) * HD * 2;
-  if (kv_bytes > 64.0 * (1 << 20))
-    hipLaunchKernelGGL((k_attn<HD, GS, true>), grid, dim3(GS * 64), 0, s, a, chunk);
-  else
-    hipLaunchKernelGGL((k_attn<HD, GS, false>), grid, dim3(GS * 64), 0, s, a, chunk);
+  // Ring depth and load schedule by launch shape (interleaved medians against
+  // two stages issued at once after each barrier; outputs identical):
+  // - at most one workgroup per CU and >= 2048 keys per workgroup: three
+  //   stages, loads spread (batch 32 over 4096 positions 107.4 -> 102.4 us;
+  //   three stages issued at once measured 150 us);
+  // - two workgroups per CU: two stages each, loads spread (batch 4 over 65536
+  //   positions 198.3 -> 190.2 us);
+  // - otherwise two stages issued at once (short key ranges: batch 1 over 4096
+  //   positions, 160 keys per split, and batch 8 were ~0.4 us slower deeper).
+  const long wgs = static_cast<long>(grid.x) * grid.y * grid.z;
+  const int mode = wgs > 256 ? 1 : (chunk >= 2048 ? 2 : 0);
+  auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(GS * 64), 0, s, a, chunk); };
+  if (kv_bytes > 64.0 * (1 << 20)) {
+    if (mode == 2) go(k_attn<HD, GS, true, 3, true>);
+    else if (mode == 1) go(k_attn<HD, GS, true, 2, true>);
+    else go(k_attn<HD, GS, true, 2, false>);
+  } else {
+    if (mode == 2) go(k_attn<HD, GS, false, 3, true>);
+    else if (mode == 1) go(k_attn<HD, GS, false, 2, true>);
+    else go(k_attn<HD, GS, false, 2, false>);
+  }
   if (splits > 1) {
     const int pairs = a.B * a.Lq * a.H;
     hipLaunchKernelGGL((k_attn_merge<HD>), dim3((pairs + 3) / 4), dim3(256), 0, s, a, splits);
