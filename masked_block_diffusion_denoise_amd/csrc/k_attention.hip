@@ -123,6 +123,27 @@ __device__ __forceinline__ void lds_read_n<2>(const uint32_t (&a)[2], u32x4 (&f)
                : "memory");
 }
 
+// Four products on two accumulators (c0 += a0 b0, c1 += a1 b0, c0 += a2 b1,
+// c1 += a3 b1), with four fragment reads (n0..n3 <- [d0..d3]) issued first and
+// waited for at the end, so that they land under the products.
+__device__ __forceinline__ void att_quad(f32x16& c0, f32x16& c1, const u32x4& a0, const u32x4& a1, const u32x4& a2,
+                                         const u32x4& a3, const u32x4& b0, const u32x4& b1, u32x4& n0, u32x4& n1,
+                                         u32x4& n2, u32x4& n3, uint32_t d0, uint32_t d1, uint32_t d2, uint32_t d3) {
+  asm volatile(
+      "ds_read_b128 %2, %12\n\t"
+      "ds_read_b128 %3, %13\n\t"
+      "ds_read_b128 %4, %14\n\t"
+      "ds_read_b128 %5, %15\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %6, %10, %0\n\t"
+      "v_mfma_f32_32x32x16_bf16 %1, %7, %10, %1\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %8, %11, %0\n\t"
+      "v_mfma_f32_32x32x16_bf16 %1, %9, %11, %1\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "+v"(c0), "+v"(c1), "=&v"(n0), "=&v"(n1), "=&v"(n2), "=&v"(n3)
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "v"(b0), "v"(b1), "v"(d0), "v"(d1), "v"(d2), "v"(d3)
+      : "memory");
+}
+
 template <int HD, int GS, bool NT, int NB, bool SPR>
 __global__ void __launch_bounds__(GS * 64) k_attn(AttnArgs a, int chunk_len) {
   constexpr int KCH = HD / 8;              // 16-byte chunks per key row
@@ -259,35 +280,74 @@ __global__ void __launch_bounds__(GS * 64) k_attn(AttnArgs a, int chunk_len) {
       __syncthreads();
     }
 
-    // S of the SUB tiles: one accumulation chain per tile, the chains
-    // interleaved so that consecutive MFMAs are independent; fragment reads in
-    // batches of KB steps per tile (register pressure)
     f32x16 sacc[SUB];
 #pragma unroll
     for (int u = 0; u < SUB; ++u)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[u][r] = 0.f;
-    constexpr int KB = NS >= 8 ? NS / 2 : NS;
-    static_assert(NS % KB == 0, "whole batches of K fragments");
+    // hd 128: each batch of fragment reads is issued under the previous batch's
+    // products (att_quad), and the first batch of V fragments under the second
+    // half of the S product, so that the P*V products start from registers
+    // right after the softmax.  Batch 32 over 4096 positions 114.9 -> 109.2 us,
+    // batch 4 over 65536 196.7 -> 192.7 us (interleaved, outputs identical).
+    constexpr bool PIPE = HD == 128 && SUB == 2;
+    u32x4 vf0[8];  // first batch of V fragments (pipelined form)
+    if constexpr (PIPE) {
+      auto qv = [&](int s) { return __builtin_bit_cast(u32x4, qf[s]); };
+      uint32_t ka[8];
+      u32x4 kf0[8], kf1[8];
 #pragma unroll
-    for (int hs = 0; hs < NS; hs += KB) {
-      uint32_t ka[SUB * KB];
-      u32x4 kf[SUB * KB];
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int u = 0; u < SUB; ++u)
+        for (int s = 0; s < 4; ++s) ka[u * 4 + s] = sb + u * TILE + koff[s];
+      lds_read_n<8>(ka, kf0);
 #pragma unroll
-        for (int s = 0; s < KB; ++s) ka[u * KB + s] = sb + u * TILE + koff[hs + s];
-      lds_read_n<SUB * KB>(ka, kf);
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int s = 0; s < KB; ++s)
+        for (int s = 0; s < 4; ++s) ka[u * 4 + s] = sb + u * TILE + koff[4 + s];
+      att_quad(sacc[0], sacc[1], kf0[0], kf0[4], kf0[1], kf0[5], qv(0), qv(1), kf1[0], kf1[1], kf1[2], kf1[3], ka[0], ka[1],
+               ka[2], ka[3]);
+      att_quad(sacc[0], sacc[1], kf0[2], kf0[6], kf0[3], kf0[7], qv(2), qv(3), kf1[4], kf1[5], kf1[6], kf1[7], ka[4], ka[5],
+               ka[6], ka[7]);
+      if (SPR && more) issue_tile(st + NB - 1, 0);
+      uint32_t va[8];
 #pragma unroll
-        for (int u = 0; u < SUB; ++u) sacc[u] = mfma32x32x16(as_bf16x8(kf[u * KB + s]), qf[hs + s], sacc[u]);
-      // one tile of stage st + NB - 1 after each batch of the S product
-      if (SPR && more && hs / KB < SUB) issue_tile(st + NB - 1, hs / KB);
-    }
-    if (SPR && more) {
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int u = NS / KB; u < SUB; ++u) issue_tile(st + NB - 1, u);
+        for (int dd = 0; dd < 2; ++dd)
+#pragma unroll
+          for (int c = 0; c < 2; ++c) va[(u * 2 + dd) * 2 + c] = sb + u * TILE + voff + c * (HD * 32) + dd * 1024;
+      att_quad(sacc[0], sacc[1], kf1[0], kf1[4], kf1[1], kf1[5], qv(4), qv(5), vf0[0], vf0[1], vf0[2], vf0[3], va[0], va[1],
+               va[2], va[3]);
+      att_quad(sacc[0], sacc[1], kf1[2], kf1[6], kf1[3], kf1[7], qv(6), qv(7), vf0[4], vf0[5], vf0[6], vf0[7], va[4], va[5],
+               va[6], va[7]);
+      if (SPR && more) issue_tile(st + NB - 1, 1);
+    } else {
+      // S of the SUB tiles: one accumulation chain per tile, the chains
+      // interleaved so that consecutive MFMAs are independent; fragment reads in
+      // batches of KB steps per tile (register pressure)
+      constexpr int KB = NS >= 8 ? NS / 2 : NS;
+      static_assert(NS % KB == 0, "whole batches of K fragments");
+#pragma unroll
+      for (int hs = 0; hs < NS; hs += KB) {
+        uint32_t ka[SUB * KB];
+        u32x4 kf[SUB * KB];
+#pragma unroll
+        for (int u = 0; u < SUB; ++u)
+#pragma unroll
+          for (int s = 0; s < KB; ++s) ka[u * KB + s] = sb + u * TILE + koff[hs + s];
+        lds_read_n<SUB * KB>(ka, kf);
+#pragma unroll
+        for (int s = 0; s < KB; ++s)
+#pragma unroll
+          for (int u = 0; u < SUB; ++u) sacc[u] = mfma32x32x16(as_bf16x8(kf[u * KB + s]), qf[hs + s], sacc[u]);
+        // one tile of stage st + NB - 1 after each batch of the S product
+        if (SPR && more && hs / KB < SUB) issue_tile(st + NB - 1, hs / KB);
+      }
+      if (SPR && more) {
+#pragma unroll
+        for (int u = NS / KB; u < SUB; ++u) issue_tile(st + NB - 1, u);
+      }
     }
     // register r of tile u holds key k0 + u*KT + 16*(r/8) + 8*half + (r%8).
     // Only the last stage of the range and causal passes need a mask.
@@ -349,27 +409,52 @@ __global__ void __launch_bounds__(GS * 64) k_attn(AttnArgs a, int chunk_len) {
       }
     }
     l_run += lsum;
-    // O^T += V^T P^T; consecutive MFMAs go to different output blocks
-    constexpr int DH = ND > 1 ? ND / 2 : 1;  // output blocks per batch of V reads
+    if constexpr (PIPE) {
+      // O^T += V^T P^T: output blocks 0-1 from vf0, reading blocks 2-3's V
+      // fragments under those products, then blocks 2-3
+      auto pv = [&](int u, int c) { return __builtin_bit_cast(u32x4, pb[u][c]); };
+      uint32_t va[8];
+      u32x4 vf1[8];
 #pragma unroll
-    for (int d0 = 0; d0 < ND; d0 += DH) {
-      uint32_t va[SUB * 2 * DH];
-      u32x4 vf[SUB * 2 * DH];
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int u = 0; u < SUB; ++u)
+        for (int dd = 0; dd < 2; ++dd)
 #pragma unroll
-        for (int dd = 0; dd < DH; ++dd)
+          for (int c = 0; c < 2; ++c) va[(u * 2 + dd) * 2 + c] = sb + u * TILE + voff + c * (HD * 32) + (2 + dd) * 1024;
+      att_quad(o[0], o[1], vf0[0], vf0[2], vf0[1], vf0[3], pv(0, 0), pv(0, 1), vf1[0], vf1[1], vf1[2], vf1[3], va[0], va[1],
+               va[2], va[3]);
+      att_quad(o[0], o[1], vf0[4], vf0[6], vf0[5], vf0[7], pv(1, 0), pv(1, 1), vf1[4], vf1[5], vf1[6], vf1[7], va[4], va[5],
+               va[6], va[7]);
 #pragma unroll
-          for (int c = 0; c < 2; ++c)
-            va[(u * DH + dd) * 2 + c] = sb + u * TILE + voff + c * (HD * 32) + (d0 + dd) * 1024;
-      lds_read_n<SUB * 2 * DH>(va, vf);
-#pragma unroll
-      for (int u = 0; u < SUB; ++u)
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
+          for (int dd = 0; dd < 2; ++dd)
+            o[2 + dd] = mfma32x32x16(as_bf16x8(vf1[(u * 2 + dd) * 2 + c]), pb[u][c], o[2 + dd]);
+    } else {
+      // O^T += V^T P^T; consecutive MFMAs go to different output blocks
+      constexpr int DH = ND > 1 ? ND / 2 : 1;  // output blocks per batch of V reads
+#pragma unroll
+      for (int d0 = 0; d0 < ND; d0 += DH) {
+        uint32_t va[SUB * 2 * DH];
+        u32x4 vf[SUB * 2 * DH];
+#pragma unroll
+        for (int u = 0; u < SUB; ++u)
+#pragma unroll
           for (int dd = 0; dd < DH; ++dd)
-            o[d0 + dd] = mfma32x32x16(as_bf16x8(vf[(u * DH + dd) * 2 + c]), pb[u][c], o[d0 + dd]);
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+              va[(u * DH + dd) * 2 + c] = sb + u * TILE + voff + c * (HD * 32) + (d0 + dd) * 1024;
+        lds_read_n<SUB * 2 * DH>(va, vf);
+#pragma unroll
+        for (int u = 0; u < SUB; ++u)
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int dd = 0; dd < DH; ++dd)
+              o[d0 + dd] = mfma32x32x16(as_bf16x8(vf[(u * DH + dd) * 2 + c]), pb[u][c], o[d0 + dd]);
+      }
     }
   }
 
