@@ -80,6 +80,17 @@ def test_attention_batch4_prefix65536():
     run_case(4, 32, 32, 8, 128, [65536, 65533, 65530, 65527], 0, 0, seed=10, check_rows=[0, 3])
 
 
+@pytest.mark.parametrize("causal", [0, 1])
+def test_attention_three_stage_ring_ragged_poisoned(causal):
+    announce(f"attention three-stage ring, ragged poisoned tails, causal={causal}")
+    # 8 rows x 8 KV heads x 4 key splits = 256 workgroups of >= 2048 keys: the
+    # three-stage ring with spread loads.  Ragged ends inside a tile, ranges of
+    # an odd number of tiles (a one-tile last stage), an empty last split for
+    # the shortest row, and NaN/Inf past every row's end.
+    prefix = [9000, 8999, 8961, 8007, 7001, 6543, 8590, 8191]
+    run_case(8, 32, 32, 8, 128, prefix, 0, causal, seed=12, check_rows=[0, 2, 5, 7], poison=True)
+
+
 @pytest.mark.parametrize("hd,H,G", [(32, 4, 2), (128, 32, 8)])
 @pytest.mark.parametrize("causal", [0, 1])
 def test_attention_ignores_slots_past_the_end(hd, H, G, causal):

@@ -25,6 +25,8 @@ SHAPES = [(16, 256, 128), (13, 1024, 512), (32, 6144, 4096), (64, 384, 256), (32
           # more than one 128 x 128 tile per CU, at most one 192 x 128 tile per CU (ragged rows),
           # and the QKV projection of the 8B-class model at batch 32
           (1000, 4608, 256), (1024, 6144, 4096),
+          # 192 x 128 tiles whose last row tile leaves one wavefront a single live fragment (plain ring)
+          (968, 6144, 512),
           # long K with few 256 x 256 tiles: K split, weight tiles fastest in the tile order
           # (the down projection at batch 32; ragged rows over an 8-way split)
           (1024, 4096, 14336), (520, 1024, 8192),
