@@ -7,10 +7,10 @@
 // one vector.
 //
 // One tiled kernel for every shape: 256 x 256, 256 x 320 (LM head, rows split
-// evenly on the device), 256 x 128, 192 x 128, 256 x 64, 256 x 32, 128 x 128 or
-// 128 x 64 output tiles, 32- or 64-deep K stages in a ring of LDS buffers filled by direct
-// global-to-LDS loads, each wavefront a block of v_mfma_f32_32x32x16_bf16
-// tiles.  Short products (one canvas at batch 1-2) are HBM-bound: their
+// evenly on the device), 256 x 128, 192 x 128, 256 x 64, 256 x 32, 128 x 128,
+// 128 x 64 or 128 x 32 output tiles, 32- or 64-deep K stages in a ring of LDS
+// buffers filled by direct global-to-LDS loads, each wavefront a block of
+// v_mfma_f32_32x32x16_bf16 tiles.  Short products (one canvas at batch 1-2) are HBM-bound: their
 // activation rows are loaded once per workgroup and shared from LDS, their
 // weights (read once) with non-temporal loads, and when there are too few
 // weight tiles to fill the chip K is split over workgroups, the fp32 partials
@@ -866,8 +866,8 @@ static void launch_partials(const GemmArgs& h, hipStream_t s) {
     launch_tiled<EPI_SPLITK, 128, 128, 2, 2, 3, 64>(h, s);
   } else if (short_wide(h.N)) {
     // one canvas (up to 32 rows): 32-row tiles, a tenth fewer bytes per stage
-    // through LDS (the same measured for the four batch-1 projections: 0.2-0.4
-    // us each, e.g. gate/up 52.6 -> 52.2 us)
+    // through LDS (this and the 128 x 32 tile below measured 0.2-0.4 us faster
+    // on each of the four batch-1 projections, e.g. gate/up 52.6 -> 52.2 us)
     if (h.M <= 32)
       launch_tiled<EPI_SPLITK, 256, 32, 4, 1, 2, 64>(h, s);
     else
