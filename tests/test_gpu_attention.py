@@ -91,6 +91,15 @@ def test_attention_three_stage_ring_ragged_poisoned(causal):
     run_case(8, 32, 32, 8, 128, prefix, 0, causal, seed=12, check_rows=[0, 2, 5, 7], poison=True)
 
 
+@pytest.mark.parametrize("causal", [0, 1])
+def test_attention_two_workgroups_per_cu_poisoned(causal):
+    announce(f"attention two-stage spread ring, poisoned tail, causal={causal}")
+    # a prefill-shaped pass: 1024 queries (32 query blocks) x 8 KV heads x 2 key
+    # splits = 512 workgroups, two per CU, each with the two-stage ring and
+    # spread loads; causal key ranges end mid-tile, NaN/Inf past the row's end
+    run_case(1, 1024, 32, 8, 128, [5200], 0, causal, seed=13, poison=True)
+
+
 @pytest.mark.parametrize("hd,H,G", [(32, 4, 2), (128, 32, 8)])
 @pytest.mark.parametrize("causal", [0, 1])
 def test_attention_ignores_slots_past_the_end(hd, H, G, causal):
