@@ -549,7 +549,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* lds) {
         // products instead of all at once after the barrier.  With three
         // buffers (two stages in flight) on the batch-32 QKV (1024 x 6144 x
         // 4096, 192 x 128 tiles) and O (1024 x 4096 x 4096, 128 x 128) products:
-        // 68.6 -> 62.7 us and 54.2 -> 50.8 us.
+        // 68.6 -> 62.7 us and 54.2 -> 50.8 us; with four (160 and 128 KB of
+        // LDS) a further 64.6 -> 62.7 us and 52.1 -> 49.1 us.
 #pragma unroll
         for (int p = 0; p < NBUF - 1; ++p)
           if (p < nk) issue(p);
@@ -926,11 +927,11 @@ static hipError_t launch_epi(const GemmArgs& g, hipStream_t s) {
     if (g.N % 256 == 0 && (g.N / 256) * ((g.M + 255) / 256) >= 256)
       launch_tiled<EPI, 256, 256, 4, 2, 2, 64>(g, s);
     else if (t128 <= 256 && g.M > 128)  // several row tiles: MFMA-bound (O at 1024 rows 55 -> 52 us)
-      launch_tiled<EPI, 128, 128, 2, 2, 3, 64>(g, s);
+      launch_tiled<EPI, 128, 128, 2, 2, 4, 64>(g, s);
     else if (t128 <= 256)  // one row tile: HBM-bound, deeper ring (gate/up at 128 rows: 58 vs 74 us)
       launch_tiled<EPI, 128, 128, 2, 2, 3, 64>(g, s);
     else if (g.N % 192 == 0 && (g.N / 192) * ((g.M + 127) / 128) <= 256)
-      launch_tiled<EPI, 192, 128, 2, 2, 3, 64>(g, s);
+      launch_tiled<EPI, 192, 128, 2, 2, 4, 64>(g, s);
     else if (g.N % 256 == 0)
       launch_tiled<EPI, 256, 128, 4, 2, 3>(g, s);
     else
