@@ -88,13 +88,6 @@ __global__ void __launch_bounds__(256) k_commit(const float* __restrict__ conf,
   }
 
   const bool by_ent = o.rule == COMMIT_ENTROPY;
-  // rank among the masked positions by the rule's order
-  int rank = 0;
-  for (int i = 0; i < L; ++i) {
-    const float ci = lane_value(c, i), ei = lane_value(e, i);
-    const bool mi = (mball >> i) & 1ull;
-    rank += (mi && commit_better(by_ent, ci, ei, i, c, e, lane)) ? 1 : 0;
-  }
   bool chosen;
   int n;
   if (stop || st >= max_steps - 1) {
@@ -105,6 +98,15 @@ __global__ void __launch_bounds__(256) k_commit(const float* __restrict__ conf,
     if (o.rule == COMMIT_BOUND) {
       inA = mk && (c >= tb || (c >= o.min_threshold && c >= 1.f - o.scaling / static_cast<float>(lane + 2)));
     } else if (o.rule == COMMIT_ENTROPY) {
+      // rank among the masked positions by ascending entropy (the only rule
+      // that needs every position's rank; the others rank only the positions
+      // outside their qualifying set, below)
+      int rank = 0;
+      for (int i = 0; i < L; ++i) {
+        const float ci = lane_value(c, i), ei = lane_value(e, i);
+        const bool mi = (mball >> i) & 1ull;
+        rank += (mi && commit_better(by_ent, ci, ei, i, c, e, lane)) ? 1 : 0;
+      }
       // running sum of the entropies in rank order (float32, sequential)
       float total = 0.f, mine = 0.f;
       for (int r = 0; r < cnt; ++r) {
