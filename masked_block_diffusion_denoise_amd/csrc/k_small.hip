@@ -580,49 +580,68 @@ hipError_t masked_norm(const uint8_t* masked, int M, const float* x, int d, cons
 // max)) partials in a fixed order, then conf = 1 / sum_v exp(l_v - max), the
 // argmax (lowest id on ties) and optionally the entropy ln(s) - t / s go to
 // position rows[i] of the canvas.
+//
+// The partials are [tile][row] float4s, so one 128-byte line holds eight
+// consecutive rows of a tile.  Workgroups go to the eight XCDs in turn; the
+// grid is a multiple of 8 and workgroup b takes row (b % 8) * per + b / 8, so
+// each XCD merges one contiguous run of rows and reads each line through its
+// own L2 once (with rows in workgroup order every XCD fetched every line).
+__device__ __forceinline__ MaxSumIdx msi_shfl_down(MaxSumIdx a, int w) {
+  return MaxSumIdx{__shfl_down(a.m, w), __shfl_down(a.s, w), __shfl_down(a.idx, w), __shfl_down(a.t, w)};
+}
+
 __global__ void __launch_bounds__(256) k_head_merge(const float4* __restrict__ part, int n_tiles, int M,
-                                                    const int* __restrict__ rows,
+                                                    int total_rows, const int* __restrict__ rows,
                                                     const int* __restrict__ m_dev, float* __restrict__ conf,
                                                     int* __restrict__ argmax, float* __restrict__ entropy) {
   __shared__ float sm[256], ss[256], st[256];
   __shared__ int si[256];
-  const int i = blockIdx.x;
-  if (m_dev && i >= *m_dev) return;
+  const int per = gridDim.x / 8;
+  const int i = (blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (i >= total_rows || (m_dev && i >= *m_dev)) return;  // uniform per workgroup
   MaxSumIdx acc{-INFINITY, 0.f, 0x7fffffff, 0.f};
   for (int t = threadIdx.x; t < n_tiles; t += 256) {
     const float4 p = part[static_cast<size_t>(t) * M + i];
     acc = msi_combine(acc, MaxSumIdx{p.x, p.y, __float_as_int(p.z), p.w});
   }
-  sm[threadIdx.x] = acc.m;
-  ss[threadIdx.x] = acc.s;
-  st[threadIdx.x] = acc.t;
-  si[threadIdx.x] = acc.idx;
+  // pairwise tree: thread t takes t + w for w = 128, 64 through LDS, then
+  // w = 32 ... 1 within wavefront 0 by shuffles (the same pairs in the same
+  // order)
+  const int tid = threadIdx.x;
+  sm[tid] = acc.m;
+  ss[tid] = acc.s;
+  st[tid] = acc.t;
+  si[tid] = acc.idx;
   __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (static_cast<int>(threadIdx.x) < w) {
-      MaxSumIdx a{sm[threadIdx.x], ss[threadIdx.x], si[threadIdx.x], st[threadIdx.x]};
-      MaxSumIdx c{sm[threadIdx.x + w], ss[threadIdx.x + w], si[threadIdx.x + w], st[threadIdx.x + w]};
-      a = msi_combine(a, c);
-      sm[threadIdx.x] = a.m;
-      ss[threadIdx.x] = a.s;
-      st[threadIdx.x] = a.t;
-      si[threadIdx.x] = a.idx;
-    }
-    __syncthreads();
+  if (tid < 128) {
+    acc = msi_combine(acc, MaxSumIdx{sm[tid + 128], ss[tid + 128], si[tid + 128], st[tid + 128]});
+    sm[tid] = acc.m;
+    ss[tid] = acc.s;
+    st[tid] = acc.t;
+    si[tid] = acc.idx;
   }
-  if (threadIdx.x == 0) {
+  __syncthreads();
+  if (tid >= 64) return;
+  acc = msi_combine(acc, MaxSumIdx{sm[tid + 64], ss[tid + 64], si[tid + 64], st[tid + 64]});
+#pragma unroll
+  for (int w = 32; w > 0; w >>= 1) {
+    const MaxSumIdx o = msi_shfl_down(acc, w);
+    acc = msi_combine(acc, o);  // lanes >= w hold values no lane reads later
+  }
+  if (tid == 0) {
     const int dst = rows ? rows[i] : i;
-    conf[dst] = 1.0f / ss[0];
-    argmax[dst] = si[0];
-    if (entropy) entropy[dst] = logf(ss[0]) - st[0] / ss[0];
+    conf[dst] = 1.0f / acc.s;
+    argmax[dst] = acc.idx;
+    if (entropy) entropy[dst] = logf(acc.s) - acc.t / acc.s;
   }
 }
 
 hipError_t head_merge(const void* partials, int n_tiles, int M, const int* rows, const int* m_dev,
                       float* conf, int* argmax, int total_rows, hipStream_t s, float* entropy) {
   if (total_rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_head_merge, dim3(total_rows), dim3(256), 0, s, static_cast<const float4*>(partials),
-                     n_tiles, M, rows, m_dev, conf, argmax, entropy);
+  const int grid = (total_rows + 7) / 8 * 8;
+  hipLaunchKernelGGL(k_head_merge, dim3(grid), dim3(256), 0, s, static_cast<const float4*>(partials), n_tiles, M,
+                     total_rows, rows, m_dev, conf, argmax, entropy);
   return hipGetLastError();
 }
 
