@@ -30,6 +30,8 @@ SHAPES = [(16, 256, 128), (13, 1024, 512), (32, 6144, 4096), (64, 384, 256), (32
           # long K with few 256 x 256 tiles: K split, weight tiles fastest in the tile order
           # (the down projection at batch 32; ragged rows over an 8-way split)
           (1024, 4096, 14336), (520, 1024, 8192),
+          # the O projection at batch 32 (128 x 128 tiles, one per CU)
+          (1024, 4096, 4096),
           # more than one 128 x 128 or 192 x 128 tile per CU, too few 256 x 256 tiles:
           # 256 x 128 (ragged rows)
           (1000, 5120, 256),
