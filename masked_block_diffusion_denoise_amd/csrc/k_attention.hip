@@ -487,9 +487,11 @@ __global__ void __launch_bounds__(GS * 64) k_attn(AttnArgs a, int chunk_len) {
 
 // Merge split partials: o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
 // One wavefront per (row, head): lane s holds split s's (m, l); each lane sums
-// HD/64 (or one) output dims over the splits in split order, the partials of
-// eight splits loaded at once (every split's partial is written, an empty one
-// as zeros with weight 0).
+// HD/64 (or one) output dims over the splits in split order (every split's
+// partial is written, an empty one as zeros with weight 0).  The partials of the
+// first 16 splits are loaded together with the (m, l) pairs, since they do not
+// depend on them, so up to 16 splits take one memory round trip instead of
+// three; further splits follow 16 at a time.
 template <int HD>
 __global__ void __launch_bounds__(256) k_attn_merge(AttnArgs a, int splits) {
   const int rows = a.B * a.Lq;
@@ -498,6 +500,19 @@ __global__ void __launch_bounds__(256) k_attn_merge(AttnArgs a, int splits) {
   if (pair >= rows * a.H) return;
   const int mrow = pair / a.H, h = pair % a.H;
   auto at = [&](int s) { return (static_cast<size_t>(s) * rows + mrow) * a.H + h; };
+  constexpr int PER = HD >= 64 ? HD / 64 : 1;
+  constexpr int B16 = 16;
+  const int d0 = min(lane * PER, HD - PER);  // lanes past HD (HD < 64) duplicate the last dims, not stored
+  float v[B16][PER];
+  auto load = [&](int s0) {
+#pragma unroll
+    for (int k = 0; k < B16; ++k) {
+      const float* po = a.part_o + at(min(s0 + k, splits - 1)) * HD + d0;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) v[k][e] = po[e];
+    }
+  };
+  load(0);
   float2 ml = make_float2(-INFINITY, 0.f);
   if (lane < splits) ml = *reinterpret_cast<const float2*>(a.part_ml + at(lane) * 2);
   float mx = ml.y > 0.f ? ml.x : -INFINITY;
@@ -506,22 +521,13 @@ __global__ void __launch_bounds__(256) k_attn_merge(AttnArgs a, int splits) {
   const float mu = (mx == -INFINITY) ? 0.f : mx;
   const float wgt = (ml.y > 0.f) ? __builtin_amdgcn_exp2f(ml.x - mu) : 0.f;
   const float l = wave_sum(wgt * ml.y);
-  constexpr int PER = HD >= 64 ? HD / 64 : 1;
-  constexpr int B8 = 8;
   float acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-  const int d0 = min(lane * PER, HD - PER);  // lanes past HD (HD < 64) duplicate the last dims, not stored
-  for (int s0 = 0; s0 < splits; s0 += B8) {
-    float v[B8][PER];
+  for (int s0 = 0; s0 < splits; s0 += B16) {
+    if (s0 > 0) load(s0);
 #pragma unroll
-    for (int k = 0; k < B8; ++k) {
-      const float* po = a.part_o + at(min(s0 + k, splits - 1)) * HD + d0;
-#pragma unroll
-      for (int e = 0; e < PER; ++e) v[k][e] = po[e];
-    }
-#pragma unroll
-    for (int k = 0; k < B8; ++k) {
+    for (int k = 0; k < B16; ++k) {
       const float ws = __shfl(wgt, min(s0 + k, 63), WAVE);
       if (s0 + k < splits)
 #pragma unroll

@@ -334,7 +334,12 @@ __global__ void __launch_bounds__(T) k_resid_norm(const float* __restrict__ part
   const float* pr = part + static_cast<size_t>(m) * d;
   float4 v0 = make_float4(0.f, 0.f, 0.f, 0.f), v1 = v0;
   float ss = 0.f;
+  // the gains are loaded with the row, not after the block sum: one memory round
+  // trip per launch instead of two (the barrier inside block_sum would hold a
+  // later load back)
+  u32x4 graw = {0, 0, 0, 0};
   if (on) {
+    graw = ld16(g + c * 8);
     v0 = reinterpret_cast<const float4*>(xr)[2 * c];
     v1 = reinterpret_cast<const float4*>(xr)[2 * c + 1];
     const float4 a0 = sum_planes(pr + 8 * c, plane, S);
@@ -349,7 +354,7 @@ __global__ void __launch_bounds__(T) k_resid_norm(const float* __restrict__ part
   const float rstd = rsqrtf(block_sum<T>(ss, red) / d + eps);
   if (!on) return;
   float gg[8];
-  unpack8(ld16(g + c * 8), gg);
+  unpack8(graw, gg);
   u32x4 o;
   o[0] = pack_bf16x2(v0.x * rstd * gg[0], v0.y * rstd * gg[1]);
   o[1] = pack_bf16x2(v0.z * rstd * gg[2], v0.w * rstd * gg[3]);
