@@ -24,7 +24,8 @@ Sources (web pages this follows; cited by title and section):
 Pins (what each function is checked against, in tests/test_oracle_*.py):
   rms_norm, rope, attend     closed forms and hand-computed values
   forward (causal / block)   structural special cases with closed forms,
-                             cache == from-scratch recompute with an explicit mask
+                             cache == from-scratch recompute with an explicit mask,
+                             the SwiGLU FFN (its norm, gate/up roles, residual) by hand
   head_logits, confidence    hand-computed softmax values, tie and mask rules
   commit and the block loop  step counts fixed by the rule (threshold 1.0 with
                              quota 1 takes L steps; all-confident takes 1),

@@ -144,3 +144,40 @@ def test_greedy_ar_with_cache_equals_recompute():
     a = oracle.generate_ar(w, TINY, prompt, 6)
     b = oracle.generate_ar_recompute(w, TINY, prompt, 6)
     np.testing.assert_array_equal(a, b)
+
+
+def test_swiglu_ffn_by_hand():
+    # One layer with its attention switched off (wo = 0) and an FFN that reads
+    # one gate row and one up row.  The embedding row is (3, 4, 0, ..., 0) in
+    # d = 128, the FFN norm gains are 0.5 (the attention norm's stay 1, so using
+    # the wrong norm shows), gate row 0 = 0.2 e_0, up row 0 = 0.2 e_1, and the
+    # down projection writes their product to dimension 5.  By hand:
+    #   rstd = 1 / sqrt(25/128 + 1e-5)          = 2.2626838
+    #   normalised input = (3, 4) * rstd * 0.5  = (3.3940257, 4.5253676)
+    #   gate = 0.2 * 3.3940257 = 0.67880513,  up = 0.2 * 4.5253676 = 0.90507351
+    #   sigmoid(gate) = 1 / (1 + e^-0.67880513) = 0.66347196
+    #   silu(gate) * up = 0.67880513 * 0.66347196 * 0.90507351 = 0.40761630
+    # so dimension 5 becomes 0 + 0.40761630 and every other dimension keeps the
+    # embedding (the residual).  Gate and up swapped would give 0.43742487, the
+    # attention norm's gains 1.95460376.
+    shape = dataclasses.replace(TINY, n_layers=1)
+    w = synth.model_weights(shape, seed=7)
+    w = {**w, "embed": np.array(w["embed"], dtype=np.float64), "layers": [dict(w["layers"][0])]}
+    l = w["layers"][0]
+    d, f = shape.d_model, shape.d_ffn
+    tok = 9
+    w["embed"][tok] = 0.0
+    w["embed"][tok, 0], w["embed"][tok, 1] = 3.0, 4.0
+    l["wo"] = np.zeros_like(l["wo"])
+    l["attn_norm"] = np.ones(d)
+    l["ffn_norm"] = np.full(d, 0.5)
+    l["wg"] = np.zeros((f, d))
+    l["wg"][0, 0] = 0.2
+    l["wu"] = np.zeros((f, d))
+    l["wu"][0, 1] = 0.2
+    l["wd"] = np.zeros((d, f))
+    l["wd"][5, 0] = 1.0
+    x = oracle.forward(w, shape, np.array([tok]), None, mode="causal")[0]
+    want = np.zeros(d)
+    want[0], want[1], want[5] = 3.0, 4.0, 0.40761630
+    np.testing.assert_allclose(x, want, rtol=0, atol=5e-9)
