@@ -181,3 +181,35 @@ def test_swiglu_ffn_by_hand():
     want = np.zeros(d)
     want[0], want[1], want[5] = 3.0, 4.0, 0.40761630
     np.testing.assert_allclose(x, want, rtol=0, atol=5e-9)
+
+
+def test_o_proj_adapter_by_hand():
+    # The draft adapter adds scale * (o A^T) B^T to the output projection, o
+    # being the attention output (the projection's input), not the layer input.
+    # Identity attention model (values = normalised inputs, wo = I, FFN off),
+    # two tokens in causal mode, rank 1: A = e_2^T (reads o[2]), B = e_7 (writes
+    # dimension 7), scale 4.  Embedding rows: token 0 = 2 e_2, token 1 = 6 e_3
+    # (d = 128).  By hand, for token 1:
+    #   n_0 = 2 e_2 / sqrt(4/128 + 1e-5)  = 11.3118987 e_2
+    #   n_1 = 6 e_3 / sqrt(36/128 + 1e-5) = 11.3135074 e_3
+    #   o_1 = (n_0 + n_1) / 2              = 5.6559494 e_2 + 5.6567537 e_3
+    #   x_1 = 6 e_3 + o_1 + 4 * o_1[2] e_7 = 5.6559494 e_2 + 11.6567537 e_3 + 22.6237975 e_7
+    # The adapter on the token's own normalised row instead of o gives 0 in
+    # dimension 7, without its scale 5.6559494.
+    shape, w = _identity_attention_model(seed=2)
+    w = {**w, "embed": np.array(w["embed"], dtype=np.float64), "layers": [dict(w["layers"][0])]}
+    d = shape.d_model
+    w["layers"][0]["attn_norm"] = np.ones(d)
+    w["embed"][11] = 0.0
+    w["embed"][11, 2] = 2.0
+    w["embed"][12] = 0.0
+    w["embed"][12, 3] = 6.0
+    a = np.zeros((1, shape.n_heads * shape.head_dim))
+    a[0, 2] = 1.0
+    b = np.zeros((d, 1))
+    b[7, 0] = 1.0
+    lora = {"a": [a], "b": [b], "scale": 4.0}
+    x = oracle.forward(w, shape, np.array([11, 12]), None, mode="causal", lora=lora)[1]
+    want = np.zeros(d)
+    want[2], want[3], want[7] = 5.6559494, 11.6567537, 22.6237975
+    np.testing.assert_allclose(x, want, rtol=0, atol=5e-7)
