@@ -26,7 +26,8 @@ Pins (what each function is checked against, in tests/test_oracle_*.py):
   forward (causal / block)   structural special cases with closed forms,
                              cache == from-scratch recompute with an explicit mask,
                              the SwiGLU FFN (its norm, gate/up roles, residual) and the
-                             draft adapter on o_proj (its input, scale, A/B roles) by hand
+                             draft adapter on o_proj (its input, scale, A/B roles) by hand,
+                             RoPE on both queries and keys (shift invariance, order)
   head_logits, confidence    hand-computed softmax values, tie and mask rules
   commit and the block loop  step counts fixed by the rule (threshold 1.0 with
                              quota 1 takes L steps; all-confident takes 1),

@@ -213,3 +213,23 @@ def test_o_proj_adapter_by_hand():
     want = np.zeros(d)
     want[2], want[3], want[7] = 5.6559494, 11.6567537, 22.6237975
     np.testing.assert_allclose(x, want, rtol=0, atol=5e-7)
+
+
+def test_rope_makes_attention_relative_in_the_forward():
+    # Rotating both queries and keys by their positions makes every score depend
+    # only on the position difference (the rotation property of RoPE), so the
+    # forward is unchanged when every position moves by the same amount; a
+    # rotation of only one side depends on absolute positions.  And RoPE must
+    # act at all: without it, bidirectional attention would not see the order
+    # of its keys, and reversing the tokens would only reverse the outputs.
+    shape = dataclasses.replace(TINY, n_layers=1)
+    w = synth.model_weights(shape, seed=11)
+    tok = np.array([5, 77, 300, 12, 900, 41])
+    t = len(tok)
+    for mode in ("causal", "block"):
+        x0 = oracle.forward(w, shape, tok, None, mode=mode, positions=np.arange(t))
+        x1 = oracle.forward(w, shape, tok, None, mode=mode, positions=137 + np.arange(t))
+        np.testing.assert_allclose(x1, x0, rtol=0, atol=1e-9)
+    xb = oracle.forward(w, shape, tok, None, mode="block")
+    xr = oracle.forward(w, shape, tok[::-1], None, mode="block")
+    assert np.abs(xr[::-1] - xb).max() > 1e-3
