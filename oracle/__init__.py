@@ -37,11 +37,15 @@ Pins (what each function is checked against, in tests/test_oracle_*.py):
                              two-way split is the binary entropy, one dominant
                              logit tends to 0
   commit_rule, adaptive_stop hand-worked cases from the page statements
-                             (tests/golden/sampler_rules.json), the native rule
-                             equal to ``commit``, brute force over tiny cases
+                             (tests/golden/sampler_rules.json and direct cases:
+                             the bounded rule's tie at the threshold, the
+                             per-step cap), the native rule equal to ``commit``,
+                             brute force over tiny cases
   generate_linear_spec       equals generate_ar token for token (lossless), with
-                             and without the adaptive window; its trimmed cache
-                             equals a causal prefill of prompt + output
+                             and without the adaptive window, also on a
+                             hand-built model whose drafts are all rejected or
+                             all accepted; its trimmed cache equals a causal
+                             prefill of prompt + output
 Whole-model numeric values of a random-init network are not printed on any
 page: beyond the pins above, those are "parity unpinned" (self-consistency only).
 """

@@ -133,3 +133,36 @@ def test_rules_brute_force_properties():
                 assert chosen == set(sorted(A, key=key)[:want])
             else:
                 assert chosen == set(pool[:want])
+
+
+def test_bound_rule_reaches_the_global_threshold():
+    # MLX guide, sec. 5.2: under the bounded sampler a token qualifies when its
+    # confidence reaches the global threshold (0.9), or is not below min_threshold
+    # (0.45) and not below the position threshold 1 - 2 / (pos + 2).  Positions 21
+    # and 22 hold exactly 0.9 where the position threshold is above it (0.913,
+    # 0.917), so they qualify through the global threshold alone, and both open
+    # although the quota is 1; every other position (0.3) is below min_threshold.
+    L = 24
+    conf = np.full(L, 0.3, np.float32)
+    conf[21] = conf[22] = np.float32(0.9)
+    canvas = np.zeros(L, np.int64)
+    argmax = np.arange(L) + 100
+    c, m, s, n = oracle.commit_rule(conf, argmax, canvas, np.ones(L, bool), 0.9, 1, 0, 32, rule="bound")
+    assert n == 2 and np.flatnonzero(~m).tolist() == [21, 22]
+    assert c[21] == 121 and c[22] == 122 and s == 1
+
+
+def test_max_transfer_keeps_the_best_ranked_of_the_chosen():
+    # Bounded sampler, quota 2, at most 1 per step.  Position 0 (0.5) qualifies
+    # through its position threshold (1 - 2/2 = 0, and 0.5 >= 0.45); position 5
+    # (0.6) does not (1 - 2/7 = 0.714) and joins through the quota.  The cap keeps
+    # the best-ranked of the two by (-conf, position): position 5, although the
+    # qualifying set listed position 0 first.
+    L = 8
+    conf = np.full(L, 0.1, np.float32)
+    conf[0], conf[5] = 0.5, 0.6
+    canvas = np.zeros(L, np.int64)
+    argmax = np.arange(L) + 100
+    c, m, s, n = oracle.commit_rule(conf, argmax, canvas, np.ones(L, bool), 0.9, 2, 0, 32, rule="bound",
+                                    max_transfer=1)
+    assert n == 1 and np.flatnonzero(~m).tolist() == [5] and c[5] == 105

@@ -7,6 +7,8 @@ lossless by construction; generate_ar is itself pinned against recompute), the
 trimmed cache equals a causal prefill of the emitted tokens, the adaptive window
 follows the page's rule, and the LoRA term is pinned through a case where it
 cancels the output projection exactly."""
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -88,3 +90,45 @@ def test_lora_can_cancel_the_output_projection(tiny):
     zero = {"a": lora["a"], "b": [np.zeros_like(b) for b in lora["b"]], "scale": scale}
     np.testing.assert_allclose(oracle.forward(w, TINY, prompt, None, mode="block", lora=zero),
                                oracle.forward(w, TINY, prompt, None, mode="block"), rtol=0, atol=0)
+
+
+def _copy_model(next_of):
+    """One layer whose attention and FFN add nothing (wo = wd = 0), one-hot
+    embeddings (token t < d is e_t), and a head under which token t predicts
+    next_of[t]: every prediction depends only on the token at its position, in
+    the bidirectional draft and in the causal verification alike."""
+    shape = dataclasses.replace(TINY, n_layers=1)
+    w = synth.model_weights(shape, seed=3)
+    layer = dict(w["layers"][0])
+    layer["wo"] = np.zeros_like(layer["wo"])
+    layer["wd"] = np.zeros_like(layer["wd"])
+    embed = np.zeros((shape.vocab, shape.d_model))
+    embed[np.arange(shape.d_model), np.arange(shape.d_model)] = 1.0
+    head = np.zeros((shape.vocab, shape.d_model))
+    for t, nxt in next_of.items():
+        head[nxt, t] = 1.0
+    w = {**w, "layers": [layer], "embed": embed, "lm_head": head, "final_norm": np.ones(shape.d_model)}
+    return shape, w
+
+
+def test_spec_acceptance_on_a_copy_model():
+    # Every draft of a masked position is next_of[MASK] = 5.  Chain 7 -> 9 -> 11
+    # -> ...: a draft 5 is never the causal prediction, so each round accepts
+    # nothing and emits only its known token; a check of draft a against the
+    # prediction after position a + 1 (instead of a) would accept the 5s, which
+    # also predict 5.  Chain 7 -> 9 -> 5 -> 5: every draft is right, so each round
+    # of window W accepts W - 1 drafts.  Both must equal greedy AR.
+    mask = TINY.mask_id
+    lora = {"a": [np.zeros((1, TINY.n_heads * TINY.head_dim))], "b": [np.zeros((TINY.d_model, 1))], "scale": 4.0}
+    prompt = np.array([3, 7])
+    chain = {mask: 5, 5: 5, 3: 7, **{t: t + 2 for t in range(7, 40, 2)}}
+    shape, w = _copy_model(chain)
+    ar = oracle.generate_ar(w, shape, prompt, 8)
+    assert ar.tolist() == [9, 11, 13, 15, 17, 19, 21, 23]
+    out, accepted, _, _ = oracle.generate_linear_spec(w, shape, prompt, 8, lora, window=4)
+    assert out.tolist() == ar.tolist() and accepted == [0] * 8
+    shape, w = _copy_model({mask: 5, 5: 5, 3: 7, 7: 9, 9: 5})
+    ar = oracle.generate_ar(w, shape, prompt, 8)
+    assert ar.tolist() == [9, 5, 5, 5, 5, 5, 5, 5]
+    out, accepted, _, _ = oracle.generate_linear_spec(w, shape, prompt, 8, lora, window=4)
+    assert out.tolist() == ar.tolist() and accepted == [3, 3]
