@@ -140,6 +140,8 @@ def test_denoise_step_validation(model):
     assert run(Lb=65) == -2
     assert run(Lb=0) == -2
     assert run(max_prefix=120) == -3           # 120 + 16 > 128
+    assert run(max_prefix=113) == -3           # one slot past the capacity
+    assert run(max_prefix=112) == -6           # an exact fit passes, then the (empty) workspace fails
     assert run(max_prefix=-1) == -1
     assert run(canvas=None) == -1
     assert run(conf=C.c_void_p(4098)) == -1    # misaligned
@@ -167,6 +169,7 @@ def test_noalloc_step_validation_and_scratch_limit():
         assert L.NOALLOC_SCRATCH_BYTES == 64 << 20
         assert lib.dlm_workspace_bytes(h, 32 * 32, 4096 + 32) > L.NOALLOC_SCRATCH_BYTES
         assert run(32, 32, 4096) == -6                 # batch 32 needs more than 64 MiB
+        assert run(8, 32, 4096) == -6                  # batch 8 needs 71.8 MB, just over
         assert b"scratch" in lib.dlm_last_error()
     finally:
         lib.dlm_model_destroy(h)
