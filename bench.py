@@ -429,7 +429,7 @@ def blas_setup():
     return info
 
 
-def cpu_baseline(w, shape, inputs, P=4096, sample_rows=8):
+def cpu_baseline(w, shape, inputs, P=4096, sample_rows=16):
     """The oracle (float64 NumPy) on bounded samples of the configured workloads:
     the one-layer step at batch 32 (``sample_rows`` rows, scaled to the batch; the
     headline leg), the same step at batch 1, and config 1 (the tiny model) end to end."""
