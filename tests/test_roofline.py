@@ -97,3 +97,30 @@ def test_roofline_record(ms, bound):
     r = R.roofline(b, f, ms)
     assert r["bound"] == bound and r["unit"] == "TFLOP/s"
     assert r["frac"] == pytest.approx(f / (ms * 1e-3) / 2.5e15, rel=1e-3)
+
+
+# One 8B-class layer and head (d 4096, 32/8 heads of 128, SwiGLU 14336, vocab
+# 131072) over a 4096-position prefix with 32-position canvases; every operand
+# counted once, bf16 except the fp32 residual stream (read and written).
+#   lm_head:   weights V*d*2 + scored rows r*d*2;        flops 2*r*d*V
+#   attention: K and V of prefix + canvas B*4128*8*128*2*2 + q in and o out M*4096*2*2;
+#              flops 2*M*32*128*4128 for Q K^T and as much for P V
+#   qkv:       weights 6144*4096*2 + rows in M*4096*2 + q/k/v out M*6144*2
+#   o_proj:    weights 4096*4096*2 + rows in M*4096*2 + residual M*4096*4*2
+#   gate_up:   weights 28672*4096*2 + rows in M*4096*2 + SwiGLU out M*14336*2
+#   down:      weights 4096*14336*2 + rows in M*14336*2 + residual M*4096*4*2
+# (M = 32 * B canvas rows; r = 496 scored rows at batch 32, 19 at batch 1.)
+KERNEL_WORK_BY_HAND = {
+    (32, 496): {"lm_head": (1077805056, 532575944704), "attention": (557842432, 69256347648),
+                "qkv": (71303168, 51539607552), "o_proj": (75497472, 34359738368),
+                "gate_up": (272629760, 240518168576), "down": (180355072, 120259084288)},
+    (1, 19): {"lm_head": (1073897472, 20401094656), "attention": (17432576, 2164260864),
+              "qkv": (50987008, 1610612736), "o_proj": (34865152, 1073741824),
+              "gate_up": (236060672, 7516192768), "down": (119406592, 3758096384)},
+}
+
+
+@pytest.mark.parametrize("B,rows", list(KERNEL_WORK_BY_HAND))
+def test_kernel_work_by_hand(B, rows):
+    for name, (by, fl) in KERNEL_WORK_BY_HAND[(B, rows)].items():
+        assert R.kernel_work(name, B, 32, 4096, rows, **SHAPE) == (by, fl), name
