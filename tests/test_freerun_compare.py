@@ -1,7 +1,10 @@
 """The end-to-end comparison helpers on the CPU: fed the oracle's own decode
-they pass, and a planted mistake in the "device" side (a flipped token, a
-position committed out of confidence order, a remasked position) fails them.
-The cases are the ones the GPU free-running tests use."""
+they pass, and a planted mistake in the "device" side (a flipped token, also
+at the last clear step, a position committed out of confidence order, a
+remasked position, a clearly confident position left masked, a missed quota, an
+incomplete last step) fails them.  Hand-built logits check that each kind of
+near decision (threshold, selection boundary, token) is flagged as ambiguous.
+The decode cases are the ones the GPU free-running tests use."""
 import numpy as np
 import pytest
 
@@ -101,3 +104,65 @@ def test_trajectory_check_catches_planted_mistakes():
                 with pytest.raises(AssertionError):
                     run(c, m)
     assert flipped >= 10 and moved >= 5 and remasked >= 20
+
+
+def _logits(rows):
+    """[L, 8] logits, id 0 the mask (-inf); each row (top, second, rest): token 1
+    scores top, token 2 second, tokens 3-7 rest."""
+    out = np.full((len(rows), 8), -np.inf)
+    for i, (top, second, rest) in enumerate(rows):
+        out[i, 1], out[i, 2], out[i, 3:] = top, second, rest
+    return out
+
+
+def test_step_ambiguity_flags_each_kind_of_near_decision():
+    from freerun import step_ambiguity
+    from oracle import confidence
+    clear = (10.0, 0.0, 0.0)                     # conf 0.9997, top-2 gap 10
+    # a masked position 0.03 from the threshold (conf 0.93: top logit 4.38 above six others)
+    lo = _logits([clear, (4.88, 0.5, 0.5), (0.0, -1.0, -1.0)])
+    conf, _ = confidence(lo)
+    assert abs(conf[1] - 0.93) < 0.01
+    assert step_ambiguity(lo, conf, np.array([1, 1, 1], bool), [0], 1, 0.9, False) == ["threshold"]
+    # the selection boundary: the committed position and the first one left 0.02 apart in
+    # log-confidence, far from the threshold and from the least confident position
+    lo = _logits([(1.02, 0.0, 0.0), (1.0, 0.0, 0.0), (0.0, 0.0, 0.0)])
+    conf, _ = confidence(lo)
+    assert step_ambiguity(lo, conf, np.array([1, 1, 1], bool), [0], 1, 0.9, False) == ["selection"]
+    # a committed token whose top two logits are 0.03 apart
+    lo = _logits([(10.0, 9.97, 0.0), clear, (0.0, -1.0, -1.0)])
+    conf, _ = confidence(lo)
+    assert step_ambiguity(lo, conf, np.array([1, 0, 1], bool), [0], 1, 0.9, True) == ["token"]
+    # all three clear: nothing flagged
+    lo = _logits([clear, (0.0, -1.0, -1.0), (-0.5, -1.0, -1.0)])
+    conf, _ = confidence(lo)
+    assert step_ambiguity(lo, conf, np.array([1, 1, 1], bool), [0], 1, 0.9, False) == []
+
+
+def test_trajectory_check_rule_violations():
+    # four masked positions: 0 and 1 clearly above the threshold, 2 and 3 far below
+    lo = _logits([(10.0, 0.0, 0.0), (9.0, 0.0, 0.0), (0.5, 0.0, 0.0), (0.0, -0.5, -0.5)])
+    M = TINY.mask_id
+    canvas, masked = np.full(4, M), np.ones(4, bool)
+    run = lambda c, m, last=False: check_trajectory_step(lo, canvas, masked, np.array(c), np.array(m, bool), 0.9,
+                                                         1, last, M)
+    assert run([1, 1, M, M], [0, 0, 1, 1]) == 2                  # the threshold set: allowed
+    with pytest.raises(AssertionError, match="clearly above the threshold"):
+        run([1, M, M, M], [0, 1, 1, 1])                           # quota met, position 1 left behind
+    with pytest.raises(AssertionError, match="quota"):
+        run([M, M, M, M], [1, 1, 1, 1])                           # nothing committed
+    assert run([1, 1, 1, 1], [0, 0, 0, 0], last=True) == 4       # last step: everything (4 clear tokens)
+    with pytest.raises(AssertionError, match="every remaining mask"):
+        run([1, 1, 1, M], [0, 0, 0, 1], last=True)                # last step leaving one masked
+
+
+@pytest.mark.parametrize("case", CLEAR[:1])
+def test_compare_checks_the_last_clear_step(case):
+    _, _, steps = decode(*case)
+    canv = [s.canvas_after.copy() for s in steps]
+    stop, _ = compare_until_ambiguity(steps, canv)
+    i = stop - 1
+    j = int(np.flatnonzero(~steps[i].masked_after)[-1])
+    canv[i][j] = (canv[i][j] + 1) % TINY.vocab or 1
+    with pytest.raises(AssertionError):
+        compare_until_ambiguity(steps, canv)
