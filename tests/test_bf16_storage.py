@@ -61,3 +61,37 @@ def test_bf16_storage_alone_exceeds_the_conf_bar_at_gain_30():
     assert B.conf_bar(np.zeros(1), np.full(1, 0.014), [0]) == 0.028
     assert out[30.0][0] > 1e-2
     assert out[30.0][1] < 0.5 * out[30.0][0]
+
+
+def test_norm_output_rounded_residual_exact():
+    # One token through an identity-attention layer (zero queries and keys, the
+    # value projection 0.3 I, the output projection I, MHA, FFN off): the
+    # attention output is the token's own stored value, so the stream must be
+    # e + bf16(0.3 bf16(RMSNorm(e))) -- the norm output and the value rounded
+    # where the device stores them, the fp32 residual sum not rounded.
+    import dataclasses
+    shape = dataclasses.replace(TINY, n_layers=1, n_kv_heads=TINY.n_heads)
+    w = synth.model_weights(shape, seed=4)
+    d = shape.d_model
+    l = dict(w["layers"][0])
+    l.update(wq=np.zeros_like(l["wq"]), wk=np.zeros_like(l["wk"]), wv=0.3 * np.eye(d), wo=np.eye(d),
+             wd=np.zeros_like(l["wd"]))
+    w = {**w, "layers": [l]}
+    tok = np.array([321])
+    e = np.asarray(w["embed"], np.float64)[tok]
+    n = oracle.model.rms_norm(e, l["attn_norm"], shape.rms_eps)
+    x16 = B.forward(w, shape, tok, oracle.KVCache(shape), "causal")
+    want = e + B.bf16(0.3 * B.bf16(n))
+    np.testing.assert_array_equal(x16, want)
+    assert not np.array_equal(want, e + B.bf16(0.3 * n))   # the norm's rounding shows
+    assert not np.array_equal(B.bf16(want), want)          # the sum itself is not a bf16 value
+    # Two tokens, causal: the second averages both stored values (equal scores),
+    # so the value rounding shows before the attention output is rounded.
+    toks = np.array([321, 77])
+    e2 = np.asarray(w["embed"], np.float64)[toks]
+    v = B.bf16(0.3 * B.bf16(oracle.model.rms_norm(e2, l["attn_norm"], shape.rms_eps)))
+    x2 = B.forward(w, shape, toks, oracle.KVCache(shape), "causal")
+    want2 = e2[1] + B.bf16((v[0] + v[1]) / 2)
+    np.testing.assert_array_equal(x2[1], want2)
+    vr = 0.3 * B.bf16(oracle.model.rms_norm(e2, l["attn_norm"], shape.rms_eps))
+    assert not np.array_equal(want2, e2[1] + B.bf16((vr[0] + vr[1]) / 2))   # the value rounding shows
