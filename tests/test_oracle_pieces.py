@@ -142,3 +142,12 @@ def test_confidence_rejects_nan():
         oracle.confidence(np.array([[0.0, np.nan]]))
     with pytest.raises(ValueError):
         oracle.confidence(np.array([[0.0, np.inf]]))
+
+
+def test_attend_refuses_a_query_that_sees_no_key():
+    # softmax over no visible key is 0/0: the oracle refuses it instead of returning NaN
+    q = np.ones((1, 2, 4))
+    k = v = np.ones((1, 3, 4))
+    allowed = np.array([[True, False, False], [False, False, False]])
+    with pytest.raises(ValueError):
+        oracle.attend(q, k, v, allowed)
