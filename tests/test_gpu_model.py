@@ -184,6 +184,63 @@ def gpu_free_run(sess, prompt, n_blocks, max_steps, tau, on_step=None):
     return out
 
 
+@pytest.mark.parametrize("Lb", [16, 1])
+def test_tiny_ragged_prefixes_and_degenerate_masks(Lb):
+    """Denoise steps at the edges of the method: rows at different prefix lengths
+    (0 included: a row with no cached key), with every, some, one or no position
+    masked; a block of one position; a step with nothing masked (nothing is
+    scored, nothing written); and a step with no cached prefix in any row (the
+    first block of an unprompted decode).  Scored positions match the oracle;
+    conf and argmax keep their earlier values everywhere else."""
+    announce(f"tiny ragged prefixes and degenerate masks L={Lb}")
+    w = synth.model_weights(TINY, seed=0, lm_head_gain=1.0)
+    m = make(TINY, w)
+    B, T = 4, 64
+    prompt = synth.prompt(TINY, B, T, seed=5)
+    sess = R.Session(m, B, 192, Lb)
+    sess.prefill(i32(prompt))
+    pre = np.array([0, 5, 40, 64])
+    sess.prefix.copy_(i32(pre))                 # the host bound max_prefix stays T
+    tok = synth.prompt(TINY, B, Lb, seed=6)
+    masked = np.zeros((B, Lb), bool)
+    masked[0] = True                            # every position
+    masked[2, ::3] = True                       # some
+    masked[3, Lb // 2] = True                   # one; row 1: none
+    canvas = np.where(masked, TINY.mask_id, tok)
+    logits = torch.zeros(B * Lb, TINY.vocab, dtype=torch.float32, device="cuda")
+
+    def step(canvas, masked, with_logits=True):
+        sess.canvas.copy_(i32(canvas))
+        sess.masked.copy_(u8(masked))
+        sess.conf.fill_(-7.0)
+        sess.argmax.fill_(-7)
+        logits.zero_()
+        sess.denoise_step(logits if with_logits else None)
+        sync()
+        return host(sess.conf), host(sess.argmax), host(logits).reshape(B, Lb, -1)
+
+    conf_g, arg_g, lg = step(canvas, masked)
+    for b in range(B):
+        mk = masked[b]
+        if mk.any():
+            cache = oracle.prefill(w, TINY, prompt[b, :pre[b]])[0] if pre[b] else oracle.KVCache(TINY)
+            check_step(conf_g[b], arg_g[b], lg[b], oracle.denoise_logits(w, TINY, cache, canvas[b]), mk)
+        assert (conf_g[b, ~mk] == -7.0).all() and (arg_g[b, ~mk] == -7).all(), b
+        assert (lg[b, ~mk] == 0).all(), b
+    # nothing masked anywhere: no position is scored or written
+    conf_g, arg_g, lg = step(tok, np.zeros((B, Lb), bool))
+    assert (conf_g == -7.0).all() and (arg_g == -7).all() and (lg == 0).all()
+    # no cached prefix in any row, every position masked: every row scores the same canvas
+    sess.prefix.zero_()
+    sess.max_prefix = 0
+    full = np.full((B, Lb), TINY.mask_id)
+    conf_g, arg_g, lg = step(full, np.ones((B, Lb), bool))
+    lo = oracle.denoise_logits(w, TINY, oracle.KVCache(TINY), full[0])
+    for b in range(B):
+        check_step(conf_g[b], arg_g[b], lg[b], lo, np.ones(Lb, bool))
+    assert (host(sess.flags) == 0).all()
+
+
 @pytest.mark.parametrize("case", freerun_cases.CLEAR)
 def test_tiny_free_running_identical_to_oracle(case):
     """Clear cases (every oracle decision more than 5e-2 from another one): the
