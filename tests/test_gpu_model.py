@@ -184,11 +184,11 @@ def gpu_free_run(sess, prompt, n_blocks, max_steps, tau, on_step=None):
     return out
 
 
-@pytest.mark.parametrize("Lb", [16, 1])
+@pytest.mark.parametrize("Lb", [16, 1, 64])
 def test_tiny_ragged_prefixes_and_degenerate_masks(Lb):
     """Denoise steps at the edges of the method: rows at different prefix lengths
     (0 included: a row with no cached key), with every, some, one or no position
-    masked; a block of one position; a step with nothing masked (nothing is
+    masked; blocks of one position and of the 64 the entry point allows; a step with nothing masked (nothing is
     scored, nothing written); and a step with no cached prefix in any row (the
     first block of an unprompted decode).  Scored positions match the oracle;
     conf and argmax keep their earlier values everywhere else."""
