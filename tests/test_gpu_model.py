@@ -241,6 +241,48 @@ def test_tiny_ragged_prefixes_and_degenerate_masks(Lb):
     assert (host(sess.flags) == 0).all()
 
 
+@pytest.mark.parametrize("Lb", [16, 1])
+def test_tiny_append_block_ragged_prefixes(Lb):
+    """dlm_append_block with every row at its own prefix length (0 included):
+    each row's block lands in cache slots [P_b, P_b + L), P_b advances by L, and
+    the keys/values and the causal next-token predictions equal the oracle's
+    causal pass over the row's prompt prefix followed by the block."""
+    announce(f"tiny append, ragged prefixes L={Lb}")
+    w = synth.model_weights(TINY, seed=0, lm_head_gain=20.0)
+    m = make(TINY, w)
+    B, T = 3, 64
+    prompt = synth.prompt(TINY, B, T, seed=7)
+    sess = R.Session(m, B, 192, Lb)
+    sess.prefill(i32(prompt))
+    pre = np.array([0, 7, 64])
+    sess.prefix.copy_(i32(pre))                 # the host bound max_prefix stays T
+    block = synth.prompt(TINY, B, Lb, seed=8)
+    sess.canvas.copy_(i32(block))
+    arg = torch.zeros(B, Lb, dtype=torch.int32, device="cuda")
+    conf = torch.zeros(B, Lb, dtype=torch.float32, device="cuda")
+    sess.append_block(arg, conf)
+    sync()
+    assert (host(sess.prefix) == pre + Lb).all() and sess.max_prefix == T + Lb
+    for b in range(B):
+        cache = oracle.prefill(w, TINY, prompt[b, :pre[b]])[0] if pre[b] else oracle.KVCache(TINY)
+        x = oracle.append_block(w, TINY, cache, block[b])
+        cache_close(sess, cache, b, pre[b] + Lb)
+        lo = oracle.head_logits(w, TINY, x)
+        conf_o, arg_o = oracle.confidence(lo)
+        # at this head gain bf16 storage alone moves some confidences by more
+        # than half the 1e-2 bar: the bar is then twice that
+        c16 = bf16_storage.prefill(w, TINY, prompt[b, :pre[b]]) if pre[b] else oracle.KVCache(TINY)
+        conf_16, _ = oracle.confidence(bf16_storage.head_logits(w, TINY, bf16_storage.append_block(w, TINY, c16,
+                                                                                                   block[b])))
+        bar = bf16_storage.conf_bar(conf_o, conf_16, np.arange(Lb))
+        assert np.abs(host(conf)[b] - conf_o).max() < bar, b
+        for j in range(Lb):
+            top2 = np.sort(lo[j][np.isfinite(lo[j])])[-2:]
+            if top2[1] - top2[0] > 5e-2:
+                assert host(arg)[b, j] == arg_o[j], (b, j)
+    assert (host(sess.flags) == 0).all()
+
+
 @pytest.mark.parametrize("case", freerun_cases.CLEAR)
 def test_tiny_free_running_identical_to_oracle(case):
     """Clear cases (every oracle decision more than 5e-2 from another one): the
