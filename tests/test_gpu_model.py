@@ -85,6 +85,36 @@ def test_tiny_prefill_cache_and_last_token():
     assert (host(sess.flags) == 0).all()
 
 
+@pytest.mark.parametrize("B,T,cap", [(2, 1, 64), (1, 128, 128), (3, 97, 128)])
+def test_tiny_prefill_edges(B, T, cap):
+    """Prefill at its edges: a one-token prompt, a prompt that fills the cache to
+    its capacity, a ragged length in one pass.  The cache and the last position's
+    greedy prediction equal the oracle's causal pass."""
+    announce(f"tiny prefill edges B={B} T={T} capacity={cap}")
+    w = synth.model_weights(TINY, seed=0, lm_head_gain=20.0)
+    m = make(TINY, w)
+    prompt = synth.prompt(TINY, B, T, seed=12)
+    sess = R.Session(m, B, cap, 16)
+    last_a = i32(np.zeros(B))
+    last_c = f32(np.zeros(B))
+    sess.prefill(i32(prompt), last_argmax=last_a, last_conf=last_c)
+    sync()
+    assert (host(sess.prefix) == T).all()
+    for b in range(B):
+        cache, x = oracle.prefill(w, TINY, prompt[b])
+        cache_close(sess, cache, b, T)
+        lg = oracle.head_logits(w, TINY, x[-1:])
+        c, a = oracle.confidence(lg)
+        c16 = oracle.KVCache(TINY)
+        x16 = bf16_storage.forward(w, TINY, prompt[b], c16, "causal")
+        c_16, _ = oracle.confidence(bf16_storage.head_logits(w, TINY, x16[-1:]))
+        assert abs(host(last_c)[b] - c[0]) < bf16_storage.conf_bar(c, c_16, [0]), b
+        top2 = np.sort(lg[0][np.isfinite(lg[0])])[-2:]
+        if top2[1] - top2[0] > 5e-2:
+            assert host(last_a)[b] == a[0], b
+    assert (host(sess.flags) == 0).all()
+
+
 def test_tiny_prefill_short_last_pass_stays_in_workspace():
     """A prompt of 1286 positions through a workspace sized for 428-row passes:
     428 + 428 + 428 + 2 positions, the last pass short (fewer rows, other split
