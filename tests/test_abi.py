@@ -286,3 +286,10 @@ def test_lora_adapter_validation():
         assert lib.dlm_model_enable_lora(h, 1) == -1
     finally:
         lib.dlm_model_destroy(h)
+
+
+def test_missing_library_raises_instead_of_falling_back(monkeypatch, tmp_path):
+    # the binding has no CPU or eager path: without the built library it refuses
+    monkeypatch.setattr(L, "_lib", None)
+    with pytest.raises(RuntimeError, match="no fallback"):
+        L.load(str(tmp_path / "libdlm.so"))
