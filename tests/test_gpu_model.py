@@ -313,6 +313,43 @@ def test_tiny_append_block_ragged_prefixes(Lb):
     assert (host(sess.flags) == 0).all()
 
 
+def test_tiny_block_ending_at_the_cache_capacity():
+    """A block whose last position is the cache's last slot: the denoise step and
+    the append at prefix + L == capacity match the oracle, and the next block's
+    step is refused (DLM_ERR_CAPACITY) before any device work."""
+    announce("tiny block at the cache capacity")
+    w = synth.model_weights(TINY, seed=0, lm_head_gain=1.0)
+    m = make(TINY, w)
+    B, T, Lb, cap = 2, 112, 16, 128
+    prompt = synth.prompt(TINY, B, T, seed=13)
+    sess = R.Session(m, B, cap, Lb)
+    sess.prefill(i32(prompt))
+    full = np.full((B, Lb), TINY.mask_id)
+    sess.canvas.copy_(i32(full))
+    sess.masked.copy_(u8(np.ones((B, Lb), bool)))
+    logits = torch.zeros(B * Lb, TINY.vocab, dtype=torch.float32, device="cuda")
+    sess.denoise_step(logits)
+    sync()
+    conf_g, arg_g, lg = host(sess.conf), host(sess.argmax), host(logits).reshape(B, Lb, -1)
+    block = synth.prompt(TINY, B, Lb, seed=14)
+    caches = []
+    for b in range(B):
+        cache, _ = oracle.prefill(w, TINY, prompt[b])
+        check_step(conf_g[b], arg_g[b], lg[b], oracle.denoise_logits(w, TINY, cache, full[b]), np.ones(Lb, bool))
+        oracle.append_block(w, TINY, cache, block[b])
+        caches.append(cache)
+    sess.canvas.copy_(i32(block))
+    sess.append_block()
+    sync()
+    assert (host(sess.prefix) == cap).all() and sess.max_prefix == cap
+    for b in range(B):
+        cache_close(sess, caches[b], b, cap)
+    with pytest.raises(L.DlmError) as e:
+        sess.denoise_step()
+    assert e.value.status == -3                 # DLM_ERR_CAPACITY
+    assert (host(sess.flags) == 0).all()
+
+
 @pytest.mark.parametrize("case", freerun_cases.CLEAR)
 def test_tiny_free_running_identical_to_oracle(case):
     """Clear cases (every oracle decision more than 5e-2 from another one): the
